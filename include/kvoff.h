@@ -1,0 +1,288 @@
+/*
+ * kvoff.h - C ABI of the MI355X sparse KV-cache offloading hot path.
+ *
+ * One decode step of one attention layer over a KV cache held mostly in
+ * pinned host DRAM, after PulseInfer ("PulseInfer: I/O-Centric Sparse KV
+ * Cache Offloading for Efficient Long-Context LLM Decoding", abstract: most
+ * historical KV blocks are stored in CPU DRAM and only selected blocks are
+ * recalled on demand; SoloHead selection and a gather-scatter I/O engine
+ * coalesce the fragmented transfers that per-head selection causes):
+ *
+ *   kvoff_offload_blocks  build per-block key digests in HBM and write the
+ *                         KV blocks to the pinned host store
+ *   kvoff_select          score every block and take one top-k block set
+ *                         per request (SoloHead) or per KV head (headwise)
+ *   kvoff_recall          move the selected, non-resident blocks host->HBM
+ *   kvoff_sparse_decode   GQA decode attention over the recalled blocks
+ *   kvoff_step            select, recall and attend over a range of layers,
+ *                         recall of layer l+1 overlapped with attention of l
+ *
+ * Block scoring.  The pages leave the per-(head, block) importance S(h, b)
+ * undefined ("PulseInfer Guide: I/O-Centric Sparse KV Cache Offloading",
+ * aiFetchly, section "SoloHead Sparse Selection").  The rule fixed here:
+ *   digest D[b][g][j] = fp32 rounding of the mean, over the valid tokens of
+ *                       block b, of key K[t][g][j] (fp64 sum, one division)
+ *   score  S[b]       = sum over query heads h and dims j of
+ *                       q[h][j] * D[b][floor(h/G)][j], in fp64
+ *   headwise S_g[b]   = the same sum over the G heads of KV head g.
+ * Selection keeps the min(k, nb) largest scores (ties: lower block id; -0.0
+ * equals +0.0) and lists them in ascending block order.
+ *
+ * Conventions for every call.
+ *   - Returns 0 (KVOFF_OK) or a negative KVOFF_E* status; no call throws.
+ *     kvoff_last_error() gives a thread-local message for the last failure.
+ *   - Device buffers are plain device pointers owned by the caller; no call
+ *     allocates device memory after kvoff_create.  Streams are hipStream_t
+ *     values passed as void* (NULL = the null stream).
+ *   - Calls enqueue work and return; outputs are valid once the stream has
+ *     synchronised.  Exceptions: kvoff_register_request and kvoff_create are
+ *     synchronous; kvoff_recall with KVOFF_ENGINE_DMA and any call given a
+ *     non-NULL kvoff_stats synchronise the stream they run on.
+ *   - Dtype of q, K, V: IEEE fp16 or bf16 (the context's dtype).
+ *     head_dim must be 128; block_size 16 or 32 tokens.
+ *   - Non-finite inputs give undefined results (not scanned).
+ *   - A context may be used from one host thread at a time.
+ */
+#ifndef KVOFF_H
+#define KVOFF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  KVOFF_OK = 0,
+  KVOFF_EINVAL = -1, /* invalid argument or shape                          */
+  KVOFF_ENOMEM = -2, /* host (pinned) allocation failed                    */
+  KVOFF_ENODEV = -3, /* no usable GPU                                      */
+  KVOFF_EHIP = -4,   /* a HIP runtime call failed (message in last_error)  */
+  KVOFF_ERANGE = -5, /* a capacity, batch or buffer size is exceeded       */
+  KVOFF_ESTATE = -6  /* e.g. a (layer, request) read before it was offloaded */
+};
+
+enum { KVOFF_F16 = 1, KVOFF_BF16 = 2 };
+
+/* selection modes */
+enum {
+  KVOFF_SOLOHEAD = 0, /* one block set per request, shared by all heads     */
+  KVOFF_HEADWISE = 1  /* one block set per KV head (fragmentation baseline) */
+};
+
+/* recall engines */
+enum {
+  /* one HIP kernel reads the mapped pinned store over the host link and
+     writes the HBM slots; the plan stays on the GPU, no host round trip */
+  KVOFF_ENGINE_ZEROCOPY = 0,
+  /* the selection is copied to the host, which issues one hipMemcpyAsync per
+     coalesced run (per (block, KV head) slice in headwise mode) on the
+     stream; synchronises that stream first */
+  KVOFF_ENGINE_DMA = 1
+};
+
+/* kind of pinned host memory for the store */
+enum {
+  KVOFF_HOST_COHERENT = 0,   /* fine-grained (hipHostMallocCoherent)      */
+  KVOFF_HOST_NONCOHERENT = 1 /* coarse-grained (hipHostMallocNonCoherent) */
+};
+
+/* largest batch one call accepts */
+#define KVOFF_MAX_BATCH 128
+
+typedef struct kvoff_ctx kvoff_ctx;
+
+typedef struct kvoff_config {
+  int32_t num_layers;           /* layers the store holds                        */
+  int32_t num_q_heads;          /* Hq; a multiple of num_kv_heads                 */
+  int32_t num_kv_heads;         /* Hkv; G = Hq/Hkv must be 1, 2, 4, 8 or 16      */
+  int32_t head_dim;             /* d; must be 128                                 */
+  int32_t block_size;           /* bs tokens per block: 16 or 32                  */
+  int32_t dtype;                /* KVOFF_F16 or KVOFF_BF16                        */
+  int32_t max_requests;         /* registrations the context accepts              */
+  int32_t host_mem_kind;        /* KVOFF_HOST_COHERENT or KVOFF_HOST_NONCOHERENT  */
+  int64_t host_capacity_blocks; /* block records the pinned store holds, summed
+                                   over layers and requests                       */
+} kvoff_config;
+
+/* Transfer statistics of one recall (or of a whole kvoff_step). */
+typedef struct kvoff_stats {
+  int64_t selected;        /* selected (block) or (block, KV head) entries     */
+  int64_t pool_hits;       /* of those, already resident in the HBM pool       */
+  int64_t items_recalled;  /* records (slices in headwise mode) moved          */
+  int64_t transfers;       /* coalesced transfers: maximal runs of consecutive
+                              missing blocks (one per slice in headwise mode) */
+  int64_t bytes;           /* bytes moved host -> HBM                          */
+} kvoff_stats;
+
+/* ------------------------------------------------------------- lifecycle */
+
+/* Validates cfg, selects the current HIP device and allocates the pinned host
+ * store (host_capacity_blocks records of 2*Hkv*bs*d*es bytes, the record size
+ * of the guide's simulator, GatherScatterEngine) plus a small device request
+ * table.  *out receives the context.  Errors: EINVAL, ENODEV, ENOMEM, EHIP. */
+int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out);
+
+/* Frees the store and the context; waits for the device first.  NULL is a no-op. */
+int kvoff_destroy(kvoff_ctx* ctx);
+
+/* Bytes of one block record: 2 * Hkv * bs * d * es. */
+int64_t kvoff_record_bytes(const kvoff_ctx* ctx);
+
+/* Reserves store capacity for a request of n_tokens tokens in every layer
+ * (nb = ceil(n_tokens / bs) records per layer) and returns its id in
+ * *req_id.  Synchronous.  Errors: EINVAL (n_tokens < 1), ERANGE (store or
+ * request table full), EHIP. */
+int kvoff_register_request(kvoff_ctx* ctx, int64_t n_tokens, int32_t* req_id);
+
+/* Host address of the record of (layer, req_id, block) in the pinned store,
+ * laid out as [Hkv][K,V][bs][d] elements.  For inspection and tests. */
+int kvoff_host_record(kvoff_ctx* ctx, int32_t layer, int32_t req_id, int64_t block,
+                      const void** ptr);
+
+/* --------------------------------------------------------------- offload */
+
+/* Digest and offload one (layer, request).
+ *   k_dev, v_dev  [n_tokens][Hkv][d] keys and values in HBM (the request's
+ *                 registered n_tokens), dtype of the context
+ *   digest_dev    out: [nb][Hkv][d] fp32 digests in HBM
+ * Writes every block record (K rows then V rows of each KV head; rows past
+ * the context end are zero) into the pinned store through its mapped
+ * address.  Errors: EINVAL, ERANGE (layer), ESTATE (unknown request), EHIP. */
+int kvoff_offload_blocks(kvoff_ctx* ctx, int32_t layer, int32_t req_id, const void* k_dev,
+                         const void* v_dev, float* digest_dev, void* stream);
+
+/* ---------------------------------------------------------------- select */
+
+/* Score and select for a batch of n_req requests (n_req <= KVOFF_MAX_BATCH).
+ *   req_ids       host [n_req] registered request ids
+ *   q_dev         [n_req][Hq][d] decode queries
+ *   digest_dev    [n_req][digest_stride][Hkv][d] fp32: request r's digests
+ *                 start at r * digest_stride blocks (digest_stride >= nb_r)
+ *   topk          host [n_req] block budgets k_r >= 1 (k_r > nb_r takes all)
+ *   mode          KVOFF_SOLOHEAD or KVOFF_HEADWISE
+ *   scores_dev    out: fp64 scores, [n_req][digest_stride] (SoloHead) or
+ *                 [n_req][Hkv][digest_stride] (headwise); entries past nb_r
+ *                 are not written
+ *   sel_idx_dev   out: [n_req][k_stride] (SoloHead) or [n_req][Hkv][k_stride]
+ *                 int32 selected block ids, ascending; unused entries -1
+ *   sel_cnt_dev   out: [n_req] int32 K_r = min(k_r, nb_r)
+ *   k_stride      row stride of sel_idx; must be >= every K_r
+ * Errors: EINVAL (k_r < 1, bad mode/sizes), ERANGE (k_stride < K_r,
+ * n_req > KVOFF_MAX_BATCH), ESTATE (unregistered request), EHIP. */
+int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* req_ids,
+                 const void* q_dev, const float* digest_dev, int64_t digest_stride,
+                 const int32_t* topk, int32_t mode, double* scores_dev, int32_t* sel_idx_dev,
+                 int32_t* sel_cnt_dev, int32_t k_stride, void* stream);
+
+/* ---------------------------------------------------------------- recall */
+
+/* Recall the selected blocks of one layer into the HBM slot pool.
+ *   slot_pool_dev [n_slots] records of kvoff_record_bytes() each, in HBM
+ *   recall_base_slot  first slot of the recall region: the record of rank i
+ *                 of request r goes to slot recall_base_slot + r*k_stride + i
+ *                 (headwise: KV head g's slice of that slot), so consecutive
+ *                 ranks land in consecutive slots and each coalesced run is
+ *                 one contiguous copy on both sides
+ *   pool_hit_dev  nullable [n_req][pool_stride] uint8: 1 where block b of
+ *                 request r is already resident in the pool at slot
+ *                 pool_slot_dev[r*pool_stride + b]; resident blocks are not moved
+ *   block_table_dev out: SoloHead [n_req][k_stride] slot of each rank;
+ *                 headwise [n_req][Hkv][k_stride] slice index (slot*Hkv + g);
+ *                 unused entries -1
+ *   engine        KVOFF_ENGINE_ZEROCOPY or KVOFF_ENGINE_DMA
+ *   stats         nullable; when given, filled after synchronising the stream
+ * Errors: EINVAL, ERANGE (recall region past n_slots), ESTATE (layer of a
+ * request not offloaded), EHIP. */
+int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* req_ids,
+                 int32_t mode, const int32_t* sel_idx_dev, const int32_t* sel_cnt_dev,
+                 int32_t k_stride, const uint8_t* pool_hit_dev, const int32_t* pool_slot_dev,
+                 int64_t pool_stride, void* slot_pool_dev, int64_t n_slots,
+                 int64_t recall_base_slot, int32_t* block_table_dev, int32_t engine,
+                 kvoff_stats* stats, void* stream);
+
+/* --------------------------------------------------------------- attention */
+
+/* Sparse GQA decode attention over the recalled blocks.
+ *   q_dev         [n_req][Hq][d]
+ *   block_table_dev, sel_idx_dev, sel_cnt_dev, k_stride: as produced by
+ *                 kvoff_recall / kvoff_select (sel_idx gives each entry's
+ *                 block id, so a request's partial last block is masked)
+ *   scale         logit scale (1/sqrt(d) for standard attention)
+ *   out_dev       out: [n_req][Hq][d] fp32
+ *   ws_dev        scratch of at least kvoff_workspace_size(ctx,
+ *                 KVOFF_CALL_SPARSE_DECODE, n_req, k_stride, mode) bytes
+ * Head h reads KV head floor(h/G).  Errors: EINVAL, ERANGE (ws too small),
+ * ESTATE, EHIP. */
+int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, int32_t mode,
+                        const void* q_dev, const void* slot_pool_dev,
+                        const int32_t* block_table_dev, const int32_t* sel_idx_dev,
+                        const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
+                        float* out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
+enum { KVOFF_CALL_SPARSE_DECODE = 1, KVOFF_CALL_STEP = 2 };
+
+/* Scratch bytes a call needs for the given batch (0 if none). */
+size_t kvoff_workspace_size(const kvoff_ctx* ctx, int32_t call, int32_t n_req,
+                            int32_t k_stride, int32_t mode);
+
+/* ------------------------------------------------------------------ step */
+
+/* Select, recall and attend for layers [layer_begin, layer_end) of one batch.
+ * Per-layer arrays are indexed by layer - layer_begin.  Two buffer sets
+ * (index 0/1) alternate between consecutive layers: select of layer l+1 is
+ * enqueued on the compute stream ahead of attention of layer l, recall runs
+ * on the copy stream as soon as its selection is ready, so the host link
+ * stays busy while attention trails one layer behind (the single-GPU form of
+ * the guide's one-layer-ahead prefetch, section "The Fallacy of Naive
+ * Offloading", and of its layer-wise scheduling).  With copy_stream equal to
+ * compute_stream the layers run serially.  Outputs equal a serial run bit
+ * for bit. */
+typedef struct kvoff_step_args {
+  int32_t layer_begin, layer_end;
+  int32_t n_req;
+  const int32_t* req_ids;            /* host [n_req]                          */
+  const int32_t* topk;               /* host [n_req]                          */
+  int32_t mode, engine, k_stride;
+  const void* const* q_dev;          /* [layers] -> [n_req][Hq][d]            */
+  const float* const* digest_dev;    /* [layers] -> digests (see kvoff_select) */
+  int64_t digest_stride;
+  const uint8_t* const* pool_hit_dev;  /* nullable; [layers] -> hit maps     */
+  const int32_t* const* pool_slot_dev; /* nullable; [layers] -> pool slots   */
+  int64_t pool_stride;
+  void* slot_pool_dev;
+  int64_t n_slots;
+  int64_t recall_base_slot[2];       /* recall region of buffer set 0 / 1      */
+  double* scores_dev[2];
+  int32_t* sel_idx_dev[2];
+  int32_t* sel_cnt_dev[2];
+  int32_t* block_table_dev[2];
+  float scale;
+  float* const* out_dev;             /* [layers] -> [n_req][Hq][d] fp32        */
+  void* ws_dev;                      /* kvoff_workspace_size(KVOFF_CALL_STEP)  */
+  size_t ws_bytes;
+  void* compute_stream;
+  void* copy_stream;
+  kvoff_stats* stats;                /* nullable: summed over layers; syncs    */
+} kvoff_step_args;
+
+int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* args);
+
+/* ------------------------------------------------------------- diagnostics */
+
+/* Reads n_bytes (a multiple of 4096) of host memory at host_ptr (pinned,
+ * from hipHostMalloc) with a GPU kernel over the host link and writes a
+ * reduction to dev_sink (>= 4096 bytes): a probe of the link's read rate for
+ * the zero-copy engine.  n_wg workgroups (0 = default). */
+int kvoff_probe_host_read(const void* host_ptr, int64_t n_bytes, void* dev_sink, int32_t n_wg,
+                          void* stream);
+
+const char* kvoff_strerror(int status);
+const char* kvoff_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,325 @@
+// attend.hip - sparse GQA decode attention over recalled blocks
+// (kvoff_sparse_decode).
+//
+// The pages describe the attention only as SoloHead-aligned sparse attention
+// over the paged KV pool ("PulseInfer Guide", aiFetchly, architecture
+// figure, section "PulseInfer Architectural Foundations").  What is computed:
+//   o[h] = sum_t softmax_t(scale * <q[h], K[t][g]>) V[t][g],  g = floor(h/G),
+// over the valid tokens t of the selected blocks of the request (headwise:
+// of the blocks KV head g selected), fp32 accumulation, fp32 output.
+//
+// Design (split-K flash decoding, one workgroup per (request, KV head,
+// split), 4 waves, each wave an independent online-softmax worker over
+// `bpw` consecutive selected blocks):
+//   QK   v_mfma_f32_16x16x32_{bf16,f16}: A = 16 tokens x 32 dims of the K
+//        tile loaded straight from HBM (each lane 16 contiguous bytes, four
+//        lanes cover 64 contiguous bytes of a token row), B = the G query
+//        heads of the group (columns >= G are zero).  The result gives lane
+//        (quad, col) the logits of tokens quad*4..quad*4+3 for head col.
+//   softmax  running max / sum per head in the log2 domain, reduced across
+//        the four quads with lane shuffles; probabilities go to LDS.
+//   PV   fp32 VALU: lane (token group quad, dim group col) loads 16 bytes of
+//        V rows t = quad + 4k and accumulates o[h][8 dims] for all G heads.
+// The four waves merge in LDS; one partial (m, l, o[128]) per (head, split)
+// goes to the workspace and combine_kernel merges splits in fixed order, so
+// results are deterministic.
+#include "kvoff_internal.h"
+
+namespace kvoff {
+namespace {
+
+constexpr int ATT_WAVES = 4;
+constexpr int PART = 2 + kHeadDim;  // m, l, o[128]
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+struct AttendArgs {
+  BatchIds batch;
+  const ReqDev* reqs;
+  const uint16_t* q;
+  const uint8_t* pool;
+  const int32_t* table;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  float* part;
+  int64_t slice_bytes;
+  int32_t k_stride, S, bpw, Hq, Hkv, hw;
+  float scale_log2;
+};
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma16x16x32(uint4 a, uint4 b, f32x4_t c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void unpack8(uint4 w, float f[8]) {
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (BF16) {
+      f[2 * e] = __uint_as_float(x[e] << 16);
+      f[2 * e + 1] = __uint_as_float(x[e] & 0xffff0000u);
+    } else {
+      f[2 * e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(x[e] & 0xffffu));
+      f[2 * e + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(x[e] >> 16));
+    }
+  }
+}
+
+template <int G, int BS, bool BF16>
+__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+  constexpr int D = kHeadDim;
+  constexpr int TILES = BS / 16;
+  __shared__ float p_s[ATT_WAVES][BS][G];
+  __shared__ float alpha_s[ATT_WAVES][G];
+  __shared__ float wm[ATT_WAVES][G], wl[ATT_WAVES][G];
+  __shared__ float wo[ATT_WAVES][G][D];
+
+  const int s = blockIdx.x % a.S;
+  const int rg = blockIdx.x / a.S;
+  const int g = rg % a.Hkv;
+  const int r = rg / a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int quad = lane >> 4, col = lane & 15;
+
+  const ReqDev rq = a.reqs[a.batch.id[r]];
+  const int cnt = a.sel_cnt[r];
+  const int64_t row = a.hw ? ((int64_t)r * a.Hkv + g) * a.k_stride : (int64_t)r * a.k_stride;
+  const int i0 = (s * ATT_WAVES + wave) * a.bpw;
+  const int i1 = min(i0 + a.bpw, cnt);
+
+  // B fragments: query head g*G + col, dims m*32 + quad*8 .. +7
+  uint4 qf[4];
+  {
+    const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + col) * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      qf[m] = col < G ? *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;  // head col's running max (log2) and sum
+  float o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+
+  for (int i = i0; i < i1; ++i) {
+    const int blk = a.sel_idx[row + i];
+    const int64_t ent = a.table[row + i];
+    const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
+    const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
+    const uint16_t* Vp = Kp + BS * D;
+    const int n_valid = (int)min<int64_t>(BS, (int64_t)rq.n_tokens - (int64_t)blk * BS);
+    if (ent < 0 || blk < 0 || n_valid <= 0) continue;  // not a valid entry: nothing to read
+
+    uint4 kf[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        kf[t][m] = *reinterpret_cast<const uint4*>(Kp + (t * 16 + col) * D + m * 32 + quad * 8);
+    uint4 vf[BS / 4];
+#pragma unroll
+    for (int k = 0; k < BS / 4; ++k)
+      vf[k] = *reinterpret_cast<const uint4*>(Vp + (quad + 4 * k) * D + col * 8);
+
+    float z[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = mfma16x16x32<BF16>(kf[t][m], qf[m], acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = t * 16 + quad * 4 + v;
+        z[t][v] = tok < n_valid ? acc[v] * a.scale_log2 : -INFINITY;
+      }
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) bm = fmaxf(bm, z[t][v]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = exp2f(m_run - m_new);
+    float ps = 0.f;
+    wave_sync_lds();
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = exp2f(z[t][v] - m_new);
+        ps += p;
+        if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
+      }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
+    wave_sync_lds();
+
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float al = alpha_s[wave][h];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= al;
+    }
+#pragma unroll
+    for (int k = 0; k < BS / 4; ++k) {
+      float vv[8];
+      unpack8<BF16>(vf[k], vv);
+      const int t = quad + 4 * k;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = p_s[wave][t][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+      }
+    }
+  }
+
+  // sum the four token groups of the wave
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      o[h][e] += __shfl_xor(o[h][e], 16);
+      o[h][e] += __shfl_xor(o[h][e], 32);
+    }
+  if (quad == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wo[wave][h][col * 8 + e] = o[h][e];
+    if (col < G) {
+      wm[wave][col] = m_run;
+      wl[wave][col] = l_run;
+    }
+  }
+  __syncthreads();
+
+  // merge the waves and write one partial per (head, split)
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, j = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) M = fmaxf(M, wm[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) {
+      const float f = wm[w][h] == -INFINITY ? 0.f : exp2f(wm[w][h] - M);
+      L = fmaf(wl[w][h], f, L);
+      O = fmaf(wo[w][h][j], f, O);
+    }
+    float* P = a.part + (((int64_t)r * a.Hq + (int64_t)g * G + h) * a.S + s) * PART;
+    if (j == 0) {
+      P[0] = M;
+      P[1] = L;
+    }
+    P[2 + j] = O;
+  }
+}
+
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, float* out, int S) {
+  const int64_t rh = blockIdx.x;  // request * Hq + head
+  const int j = threadIdx.x;
+  const float* P = part + rh * S * PART;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, P[s * PART]);
+  float L = 0.f, O = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float m = P[s * PART];
+    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
+    L = fmaf(P[s * PART + 1], f, L);
+    O = fmaf(P[s * PART + 2 + j], f, O);
+  }
+  out[rh * kHeadDim + j] = L > 0.f ? O / L : 0.f;
+}
+
+int attend_bpw(int32_t k_stride) { return k_stride <= 128 ? 2 : 4; }
+
+template <int G, int BS>
+void launch_g_bs(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL((attend_kernel<G, BS, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attend_kernel<G, BS, false>), grid, dim3(256), 0, s, a);
+}
+
+template <int G>
+void launch_g(const AttendArgs& a, int bs, bool bf16, dim3 grid, hipStream_t s) {
+  if (bs == 16)
+    launch_g_bs<G, 16>(a, bf16, grid, s);
+  else
+    launch_g_bs<G, 32>(a, bf16, grid, s);
+}
+
+}  // namespace
+
+int attend_splits(int32_t k_stride) {
+  const int per = ATT_WAVES * attend_bpw(k_stride);
+  return (k_stride + per - 1) / per;
+}
+
+size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride) {
+  return (size_t)n_req * ctx->cfg.num_q_heads * attend_splits(k_stride) * PART * sizeof(float);
+}
+
+int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,
+                  const void* pool, const int32_t* table, const int32_t* sel_idx,
+                  const int32_t* sel_cnt, int32_t k_stride, float scale, float* out, void* ws,
+                  hipStream_t stream) {
+  AttendArgs a;
+  a.batch = b;
+  a.reqs = ctx->d_reqs;
+  a.q = (const uint16_t*)q_dev;
+  a.pool = (const uint8_t*)pool;
+  a.table = table;
+  a.sel_idx = sel_idx;
+  a.sel_cnt = sel_cnt;
+  a.part = (float*)ws;
+  a.slice_bytes = ctx->slice_bytes;
+  a.k_stride = k_stride;
+  a.bpw = attend_bpw(k_stride);
+  a.S = attend_splits(k_stride);
+  a.Hq = ctx->cfg.num_q_heads;
+  a.Hkv = ctx->cfg.num_kv_heads;
+  a.hw = mode == KVOFF_HEADWISE;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)(b.n * a.Hkv * a.S));
+  const bool bf16 = ctx->cfg.dtype == KVOFF_BF16;
+  const int bs = ctx->cfg.block_size;
+  switch (ctx->G) {
+    case 1: launch_g<1>(a, bs, bf16, grid, stream); break;
+    case 2: launch_g<2>(a, bs, bf16, grid, stream); break;
+    case 4: launch_g<4>(a, bs, bf16, grid, stream); break;
+    case 8: launch_g<8>(a, bs, bf16, grid, stream); break;
+    default: launch_g<16>(a, bs, bf16, grid, stream); break;
+  }
+  KVOFF_HIP(hipGetLastError());
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
+                     a.part, out, a.S);
+  KVOFF_HIP(hipGetLastError());
+  return KVOFF_OK;
+}
+
+}  // namespace kvoff

@@ -1,0 +1,123 @@
+// kvoff_internal.h - context, error plumbing and kernel launchers shared by
+// the library's translation units.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/kvoff.h"
+
+namespace kvoff {
+
+constexpr int kHeadDim = 128;
+
+// Per-request entry of the device request table.  The record of
+// (layer, request, block) sits at store + (rec_base + layer*nb + block) * rec_bytes.
+struct ReqDev {
+  int64_t rec_base;
+  int32_t n_tokens;
+  int32_t nb;
+};
+
+// Request ids of one call, passed by value in kernel arguments.
+struct BatchIds {
+  int32_t n;
+  int32_t id[KVOFF_MAX_BATCH];
+};
+
+struct ReqHost {
+  int64_t rec_base;
+  int64_t n_tokens;
+  int64_t nb;
+};
+
+}  // namespace kvoff
+
+struct kvoff_ctx {
+  kvoff_config cfg;
+  int device = 0;
+  int G = 1;
+  int64_t rec_bytes = 0;    // 2 * Hkv * bs * d * es
+  int64_t slice_bytes = 0;  // 2 * bs * d * es (K and V of one KV head)
+  uint8_t* store = nullptr; // pinned host store (mapped into the GPU's address space)
+  uint8_t* store_dev = nullptr;  // device-side address of the store
+  int64_t store_used = 0;   // records reserved so far
+  std::vector<kvoff::ReqHost> reqs;
+  std::vector<uint8_t> offloaded;  // [req][layer]: offload enqueued
+  kvoff::ReqDev* d_reqs = nullptr; // device copy of the request table
+  unsigned long long* d_counters = nullptr;  // recall statistics (device)
+  hipEvent_t ev_sel[2] = {nullptr, nullptr};
+  hipEvent_t ev_rec[2] = {nullptr, nullptr};
+};
+
+namespace kvoff {
+
+// thread-local message of the last failure
+void set_error(const char* fmt, ...);
+int fail(int status, const char* fmt, ...);
+
+#define KVOFF_HIP(call)                                                            \
+  do {                                                                             \
+    hipError_t e_ = (call);                                                        \
+    if (e_ != hipSuccess)                                                          \
+      return ::kvoff::fail(KVOFF_EHIP, "%s failed: %s (%s:%d)", #call,             \
+                           hipGetErrorString(e_), __FILE__, __LINE__);             \
+  } while (0)
+
+// check a batch and fill BatchIds; ESTATE for an unknown id
+int make_batch(const kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, BatchIds* out);
+
+// ---- launchers (each returns a kvoff status) ----
+
+int launch_offload(const kvoff_ctx* ctx, int32_t layer, int32_t req_id, const void* k_dev,
+                   const void* v_dev, float* digest_dev, hipStream_t stream);
+
+int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t max_nb, const void* q_dev,
+                 const float* digest_dev, int64_t digest_stride, int32_t mode, double* scores_dev,
+                 hipStream_t stream);
+
+int launch_topk(const kvoff_ctx* ctx, const BatchIds& b, const int32_t* topk_host,
+                int32_t mode, const double* scores_dev, int64_t digest_stride,
+                int32_t* sel_idx_dev, int32_t* sel_cnt_dev, int32_t k_stride,
+                hipStream_t stream);
+
+struct RecallArgs {
+  int32_t layer;
+  int32_t mode;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  int32_t k_stride;
+  const uint8_t* pool_hit;
+  const int32_t* pool_slot;
+  int64_t pool_stride;
+  uint8_t* pool;
+  int64_t recall_base_slot;
+  int32_t* table;
+};
+
+int launch_gather(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, bool count,
+                  hipStream_t stream);
+int launch_table(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a,
+                 hipStream_t stream);
+int launch_zero_counters(const kvoff_ctx* ctx, hipStream_t stream);
+
+int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, kvoff_stats* stats,
+               hipStream_t stream);
+
+// split policy of the attention kernel: number of splits per (request, KV head)
+int attend_splits(int32_t k_stride);
+size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride);
+
+int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,
+                  const void* pool, const int32_t* table, const int32_t* sel_idx,
+                  const int32_t* sel_cnt, int32_t k_stride, float scale, float* out,
+                  void* ws, hipStream_t stream);
+
+int launch_probe(const void* host_ptr, int64_t n_bytes, void* sink, int32_t n_wg,
+                 hipStream_t stream);
+
+}  // namespace kvoff

@@ -1,0 +1,138 @@
+"""Parity checks of the GPU path against the oracle (shared by the GPU tests
+and the smoke check).
+
+Bars:
+  digests            bit-exact (fp32 bits)
+  scores             |gpu - oracle| <= 1e-9 * (1 + |S|)   (both fp64)
+  selection          bit-exact ids and counts; unused entries -1
+  recalled records   bit-exact bytes; table entries point at the right slots
+  transfer counts    equal to the oracle's coalesced-run / slice counts
+  attention          max |gpu - oracle_fp32| <= 2e-3 and, per (request, head)
+                     row, max|err| / max|oracle| <= 1e-2
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_kv_cache_mean_amd as kv
+from tests import workloads
+
+ATOL = 2e-3
+ROW_RTOL = 1e-2
+
+
+def check_digests(c, l, slices):
+    D = c.digest[l].cpu().numpy()
+    for r in range(c.B):
+        sl = slices[(l, r)]
+        nb = sl.lr.rq.nb
+        got = D[r, :nb]
+        assert np.array_equal(got.view(np.uint32), sl.D.view(np.uint32)), \
+            f"digest mismatch layer {l} req {r}: {np.argwhere(got != sl.D)[:5]}"
+
+
+def check_selection(c, l, mode, bufs, slices):
+    sel = bufs.sel_idx.cpu().numpy()
+    cnt = bufs.sel_cnt.cpu().numpy()
+    sc = bufs.scores.cpu().numpy()
+    for r in range(c.B):
+        sl = slices[(l, r)]
+        K, nb = sl.K, sl.lr.rq.nb
+        assert cnt[r] == K, (l, r, cnt[r], K)
+        if mode == kv.KVOFF_SOLOHEAD:
+            assert np.allclose(sc[r, 0, :nb], sl.S, rtol=0, atol=1e-9 * (1 + np.abs(sl.S).max()))
+            assert sel[r, 0, :K].tolist() == sl.sel.tolist(), (l, r)
+            assert np.all(sel[r, 0, K:] == -1)
+        else:
+            for g in range(c.s.Hkv):
+                assert np.allclose(sc[r, g, :nb], sl.Sg[g], rtol=0,
+                                   atol=1e-9 * (1 + np.abs(sl.Sg[g]).max()))
+                assert sel[r, g, :K].tolist() == sl.sel_g[g].tolist(), (l, r, g)
+                assert np.all(sel[r, g, K:] == -1)
+
+
+def expected_transfers(c, l, mode, slices, with_pool_hits):
+    n_tr = n_items = n_hits = n_sel = 0
+    for r in range(c.B):
+        sl = slices[(l, r)]
+        hit = sl.lr.pool if with_pool_hits else None
+        sets = [sl.sel] if mode == kv.KVOFF_SOLOHEAD else list(sl.sel_g)
+        for s in sets:
+            n_sel += len(s)
+            miss = [b for b in s.tolist() if not (hit is not None and hit[b])]
+            n_items += len(miss)
+            n_hits += len(s) - len(miss)
+            if mode == kv.KVOFF_SOLOHEAD:
+                n_tr += len(oracle.runs(s, hit)[0])
+            else:
+                n_tr += oracle.headwise_transfers(s[None, :], [len(s)], hit)
+    return dict(selected=n_sel, pool_hits=n_hits, items_recalled=n_items, transfers=n_tr)
+
+
+def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats=None):
+    s = c.s
+    rec = kv.kvoff_record_bytes(c.ctx)
+    slice_b = rec // s.Hkv
+    pool = c.pool.cpu().numpy()
+    table = bufs.table.cpu().numpy()
+    base = c.recall_base[region]
+    ps = c.pool_slot[l].cpu().numpy() if with_pool_hits else None
+    for r in range(c.B):
+        sl = slices[(l, r)]
+        K = sl.K
+        hit = sl.lr.pool if with_pool_hits else np.zeros(sl.lr.rq.nb, np.uint8)
+        sets = [sl.sel] if mode == kv.KVOFF_SOLOHEAD else list(sl.sel_g)
+        for g, sset in enumerate(sets):
+            want = workloads.block_records(sl, sset.tolist())  # [K][Hkv][2][bs][d]
+            for i, b in enumerate(sset.tolist()):
+                ent = int(table[r, g, i])
+                if mode == kv.KVOFF_SOLOHEAD:
+                    exp_slot = int(ps[r, b]) if hit[b] else base + r * c.k_stride + i
+                    assert ent == exp_slot, (l, r, i, ent, exp_slot)
+                    got = pool[ent * rec:(ent + 1) * rec]
+                    assert np.array_equal(got, want[i].reshape(-1).view(np.uint8)), (l, r, i, b)
+                else:
+                    slot = int(ps[r, b]) if hit[b] else base + r * c.k_stride + i
+                    assert ent == slot * s.Hkv + g, (l, r, g, i, ent)
+                    got = pool[ent * slice_b:(ent + 1) * slice_b]
+                    assert np.array_equal(got, want[i, g].reshape(-1).view(np.uint8)), (l, r, g, i)
+            assert np.all(table[r, g, K:] == -1)
+    if stats is not None:
+        exp = expected_transfers(c, l, mode, slices, with_pool_hits)
+        for k, v in exp.items():
+            assert stats[k] == v, (k, stats[k], v)
+        item = rec if mode == kv.KVOFF_SOLOHEAD else slice_b
+        assert stats["bytes"] == exp["items_recalled"] * item
+
+
+def oracle_attention(c, l, mode, slices):
+    s = c.s
+    out = np.empty((c.B, s.Hq, s.d), np.float32)
+    for r in range(c.B):
+        sl = slices[(l, r)]
+        lr = sl.lr
+        if mode == kv.KVOFF_SOLOHEAD:
+            out[r] = oracle.attend_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, sl.sel)
+        else:
+            out[r] = oracle.attend_headwise_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, sl.sel_g)
+    return out
+
+
+def check_attention_close(got: np.ndarray, ref: np.ndarray, what=""):
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert np.isfinite(got).all(), f"non-finite attention output {what}"
+    mx = float(err.max())
+    rows = err.reshape(-1, ref.shape[-1]).max(axis=1) / \
+        np.maximum(np.abs(ref).reshape(-1, ref.shape[-1]).max(axis=1), 1e-30)
+    assert mx <= ATOL, f"max abs error {mx} > {ATOL} {what}"
+    assert float(rows.max()) <= ROW_RTOL, f"row relative error {rows.max()} > {ROW_RTOL} {what}"
+    return mx, float(rows.max())
+
+
+def check_attention(c, l, mode, bufs, slices, ref=None):
+    if ref is None:
+        ref = oracle_attention(c, l, mode, slices)
+    got = bufs.out.cpu().numpy()
+    return check_attention_close(got, ref, f"(layer {l})")

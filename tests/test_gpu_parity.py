@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, at sizes the oracle finishes in seconds (several tiles, ragged
+tails).  Full-size workloads are in test_gpu_fullsize.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_kv_cache_mean_amd as kv
+import synth
+from tests import gpu_harness as H
+from tests import parity as P
+from tests import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _slices(s, layers, reqs=None):
+    reqs = reqs or synth.request_draws(s)
+    out = {}
+    for l in layers:
+        for r, rq in enumerate(reqs):
+            out[(l, r)] = workloads.make_slice(s, l, r, rq)
+    return reqs, out
+
+
+def _case(s, layers, with_pool_hits=False, host_kind=kv.KVOFF_HOST_COHERENT, reqs=None):
+    reqs, sl = _slices(s, layers, reqs)
+    inputs = {k: v.lr for k, v in sl.items()}
+    c = H.build_case(s, inputs, layers, reqs, host_kind=host_kind, with_pool_hits=with_pool_hits)
+    return c, sl
+
+
+def _full_check(c, sl, l, mode, engine, with_pool_hits=False):
+    bufs = H.make_buffers(c, mode)
+    H.log(f"  run layer {l} mode {mode} engine {engine} hits {with_pool_hits}")
+    stats = H.run_layer(c, l, mode, bufs, engine=engine, with_pool_hits=with_pool_hits,
+                        want_stats=True)
+    torch.cuda.synchronize()
+    P.check_digests(c, l, sl)
+    P.check_selection(c, l, mode, bufs, sl)
+    P.check_recall(c, l, mode, bufs, sl, with_pool_hits=with_pool_hits, stats=stats)
+    err = P.check_attention(c, l, mode, bufs, sl)
+    return stats, err
+
+
+TINY = synth.spec(1)  # 1 request, 8/2 heads, 4096 tokens, bs 16, k 32, fp16
+
+
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+def test_tiny_config_full_parity(engine):
+    H.log(f"[tiny] engine {engine}")
+    c, sl = _case(TINY, [0])
+    try:
+        stats, err = _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, engine)
+        H.log(f"  stats {stats} attention err {err}")
+    finally:
+        H.destroy(c)
+
+
+def test_tiny_config_noncoherent_store():
+    H.log("[tiny] noncoherent host store")
+    c, sl = _case(TINY, [0], host_kind=kv.KVOFF_HOST_NONCOHERENT)
+    try:
+        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+    finally:
+        H.destroy(c)
+
+
+def test_offloaded_records_in_pinned_store():
+    H.log("[records] pinned store contents")
+    import ctypes
+    s = synth.spec(1, ctx=1000)  # 63 blocks, last one holds 8 of 16 tokens
+    c, sl = _case(s, [0])
+    try:
+        rec = kv.kvoff_record_bytes(c.ctx)
+        for b in (0, 5, 62):
+            buf = np.empty(rec, np.uint8)
+            ctypes.memmove(buf.ctypes.data, kv.kvoff_host_record(c.ctx, 0, c.rids[0], b), rec)
+            want = workloads.block_records(sl[(0, 0)], [b])[0].reshape(-1).view(np.uint8)
+            assert np.array_equal(buf, want), b
+    finally:
+        H.destroy(c)
+
+
+# ragged contexts, variable k, G = 8, bf16, clustered hot runs (the variable
+# workload's recipe at reduced context lengths)
+RAGGED = synth.spec(4, B=6, ctx_range=(700, 5000))
+
+
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+def test_ragged_variable_parity(engine):
+    H.log(f"[ragged] engine {engine}")
+    c, sl = _case(RAGGED, [0])
+    try:
+        assert any(rq.ctx % RAGGED.bs for rq in c.reqs)
+        stats, err = _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, engine)
+        H.log(f"  stats {stats} attention err {err}")
+        assert stats["transfers"] < stats["items_recalled"]  # runs were coalesced
+    finally:
+        H.destroy(c)
+
+
+# headwise vs SoloHead with a quarter of the blocks resident in the HBM pool
+HW = synth.spec(5, B=3, ctx=4096, k=16, hot=6)
+
+
+@pytest.mark.parametrize("mode", [kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+def test_headwise_and_pool_hits(mode, engine):
+    H.log(f"[headwise] mode {mode} engine {engine}")
+    c, sl = _case(HW, [0], with_pool_hits=True)
+    try:
+        stats, _ = _full_check(c, sl, 0, mode, engine, with_pool_hits=True)
+        H.log(f"  stats {stats}")
+        assert stats["pool_hits"] > 0
+    finally:
+        H.destroy(c)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 2), (16, 16), (64, 4)])
+def test_group_sizes(Hq, Hkv):
+    H.log(f"[groups] Hq {Hq} Hkv {Hkv}")
+    s = synth.spec(2, B=2, Hq=Hq, Hkv=Hkv, ctx=2000, k=12, hot=5)
+    c, sl = _case(s, [0])
+    try:
+        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+        if Hkv > 1:
+            _full_check(c, sl, 0, kv.KVOFF_HEADWISE, kv.KVOFF_ENGINE_ZEROCOPY)
+    finally:
+        H.destroy(c)
+
+
+def test_degenerate_sizes():
+    """k >= nb (take every block), k = 1, one-token and one-block contexts."""
+    H.log("[degenerate]")
+    s = synth.spec(2, B=4, ctx=100, k=1, hot=1)
+    reqs = [synth.Request(ctx=1, nb=1, k=1), synth.Request(ctx=33, nb=2, k=5),
+            synth.Request(ctx=100, nb=4, k=1), synth.Request(ctx=96, nb=3, k=3)]
+    c, sl = _case(s, [0], reqs=reqs)
+    try:
+        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+        _full_check(c, sl, 0, kv.KVOFF_HEADWISE, kv.KVOFF_ENGINE_DMA)
+    finally:
+        H.destroy(c)
+
+
+# several layers: overlapped kvoff_step must equal the serial order bit for bit
+MULTI = synth.spec(3, B=2, L=4, ctx=3000, k=20, hot=8)
+
+
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+def test_step_overlap_matches_serial_and_oracle(engine):
+    H.log(f"[step] engine {engine}")
+    layers = list(range(MULTI.L))
+    c, sl = _case(MULTI, layers)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        sets = [H.make_buffers(c, mode) for _ in range(2)]
+        outs = {l: torch.empty((c.B, MULTI.Hq, MULTI.d), dtype=torch.float32, device="cuda")
+                for l in layers}
+        compute = torch.cuda.Stream()
+        copy = torch.cuda.Stream()
+
+        def step(copy_stream, want_stats=False):
+            return kv.kvoff_step(
+                c.ctx, layer_begin=0, layer_end=len(layers), req_ids=c.rids,
+                topk=[rq.k for rq in c.reqs], mode=mode, engine=engine, k_stride=c.k_stride,
+                q=[c.q[l] for l in layers], digest=[c.digest[l] for l in layers],
+                digest_stride=c.nb_max, slot_pool=c.pool, n_slots=c.n_slots,
+                recall_base_slot=c.recall_base, scores=[b.scores for b in sets],
+                sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
+                block_table=[b.table for b in sets], scale=1.0 / math.sqrt(MULTI.d),
+                out=[outs[l] for l in layers], ws=sets[0].ws, compute_stream=compute,
+                copy_stream=copy_stream, want_stats=want_stats)
+
+        step(copy)
+        torch.cuda.synchronize()
+        overlapped = {l: outs[l].cpu().numpy().copy() for l in layers}
+        stats = step(compute, want_stats=True)  # serial: one stream
+        torch.cuda.synchronize()
+        for l in layers:
+            serial = outs[l].cpu().numpy()
+            assert np.array_equal(serial.view(np.uint32), overlapped[l].view(np.uint32)), l
+            P.check_attention_close(serial, P.oracle_attention(c, l, mode, sl), f"layer {l}")
+        exp = [P.expected_transfers(c, l, mode, sl, False) for l in layers]
+        assert stats["transfers"] == sum(e["transfers"] for e in exp)
+        assert stats["items_recalled"] == sum(e["items_recalled"] for e in exp)
+    finally:
+        H.destroy(c)
+
+
+def test_error_paths_on_device():
+    H.log("[errors]")
+    s = synth.spec(1, ctx=512, k=8, hot=2)
+    c, sl = _case(s, [0])
+    try:
+        bufs = H.make_buffers(c, kv.KVOFF_SOLOHEAD)
+        with pytest.raises(kv.KvoffError) as e:  # k_stride smaller than K
+            kv.kvoff_select(c.ctx, 0, c.rids, c.q[0], c.digest[0], c.nb_max, [8],
+                            kv.KVOFF_SOLOHEAD, bufs.scores, bufs.sel_idx, bufs.sel_cnt, 4)
+        assert e.value.status == kv.KVOFF_ERANGE
+        with pytest.raises(kv.KvoffError) as e:  # k < 1
+            kv.kvoff_select(c.ctx, 0, c.rids, c.q[0], c.digest[0], c.nb_max, [0],
+                            kv.KVOFF_SOLOHEAD, bufs.scores, bufs.sel_idx, bufs.sel_cnt, 8)
+        assert e.value.status == kv.KVOFF_EINVAL
+        with pytest.raises(kv.KvoffError) as e:  # unknown request id
+            kv.kvoff_select(c.ctx, 0, [5], c.q[0], c.digest[0], c.nb_max, [8],
+                            kv.KVOFF_SOLOHEAD, bufs.scores, bufs.sel_idx, bufs.sel_cnt, 8)
+        assert e.value.status == kv.KVOFF_ESTATE
+        with pytest.raises(kv.KvoffError) as e:  # store is full
+            kv.kvoff_register_request(c.ctx, 512)
+        assert e.value.status == kv.KVOFF_ERANGE
+        with pytest.raises(kv.KvoffError) as e:  # recall region past the pool
+            kv.kvoff_recall(c.ctx, 0, c.rids, kv.KVOFF_SOLOHEAD, bufs.sel_idx, bufs.sel_cnt,
+                            c.k_stride, None, None, 0, c.pool, c.n_slots, c.n_slots,
+                            bufs.table)
+        assert e.value.status == kv.KVOFF_ERANGE
+        with pytest.raises(kv.KvoffError) as e:  # workspace too small
+            kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, bufs.table,
+                                   bufs.sel_idx, bufs.sel_cnt, c.k_stride, 0.1, bufs.out,
+                                   bufs.ws[:4])
+        assert e.value.status == kv.KVOFF_ERANGE
+        # an empty batch is a no-op
+        kv.kvoff_select(c.ctx, 0, [], c.q[0], c.digest[0], c.nb_max, [], kv.KVOFF_SOLOHEAD,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, 8)
+        torch.cuda.synchronize()
+    finally:
+        H.destroy(c)
+
+
+def test_recall_before_offload_is_rejected():
+    H.log("[errors] recall before offload")
+    ctx = kv.kvoff_create(num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                          block_size=16, dtype=kv.KVOFF_F16, max_requests=1,
+                          host_capacity_blocks=64)
+    try:
+        rid = kv.kvoff_register_request(ctx, 256)
+        sel = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+        cnt = torch.ones((1,), dtype=torch.int32, device="cuda")
+        pool = torch.zeros(4 * kv.kvoff_record_bytes(ctx), dtype=torch.uint8, device="cuda")
+        table = torch.empty((1, 4), dtype=torch.int32, device="cuda")
+        with pytest.raises(kv.KvoffError) as e:
+            kv.kvoff_recall(ctx, 1, [rid], kv.KVOFF_SOLOHEAD, sel, cnt, 4, None, None, 0, pool, 4,
+                            0, table)
+        assert e.value.status == kv.KVOFF_ESTATE
+    finally:
+        kv.kvoff_destroy(ctx)
