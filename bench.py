@@ -1,0 +1,271 @@
+"""Benchmark of the sparse KV-offloading hot path on one MI355X.
+
+One step = one layer-step of the Llama-3-8B-shaped workload (batch 16, 32
+query / 8 KV heads, head_dim 128, 32,768-token contexts in 32-token blocks,
+top-64 blocks, bf16, 5% planted hot blocks): score + SoloHead top-k, recall
+of the selected blocks from the pinned host store into HBM, sparse GQA decode
+attention.  Steps cycle through `--layers` distinct layers (separate digests
+and host records) so no step finds its digests in the 256 MB Infinity Cache
+from the previous one.  Inputs are synthetic (seeded generator, no gap
+conditioning: that only matters for parity checks) and are resident in HBM /
+the pinned store before timing starts.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import sparse_kv_cache_mean_amd as kv  # noqa: E402
+import synth  # noqa: E402
+from tests import gpu_harness as H  # noqa: E402
+
+METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM GB/s"
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+PCIE_PEAK_GBPS = 64.0       # PCIe 5.0 x16, one direction, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=40)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--layers", type=int, default=4)
+    p.add_argument("--engine", choices=["zerocopy", "dma"], default="zerocopy")
+    p.add_argument("--host-mem", choices=["coherent", "noncoherent"], default="coherent")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def link_peaks(case):
+    """Measured host->HBM peaks: one 1 GiB pinned hipMemcpyAsync (best of 5)
+    and the zero-copy read probe over the pinned store."""
+    nbytes = 1 << 30
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_copy = 0.0
+    for _ in range(5):
+        s.record()
+        dev.copy_(host, non_blocking=True)
+        e.record()
+        e.synchronize()
+        best_copy = max(best_copy, nbytes / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del host, dev
+    # zero-copy probe: read the first GiB of the request store
+    rec = kv.kvoff_record_bytes(case.ctx)
+    base = kv.kvoff_host_record(case.ctx, 0, case.rids[0], 0)
+    n = min(nbytes, (case.reqs[0].nb * rec) // 4096 * 4096)
+    sink = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    best_probe = 0.0
+    for _ in range(5):
+        s.record()
+        kv.kvoff_probe_host_read(base, n, sink)
+        e.record()
+        e.synchronize()
+        best_probe = max(best_probe, n / (s.elapsed_time(e) * 1e-3) / 1e9)
+    return best_copy, best_probe
+
+
+def hbm_copy_peak():
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(5):
+        s.record()
+        b.copy_(a)
+        e.record()
+        e.synchronize()
+        best = max(best, 2 * n / (s.elapsed_time(e) * 1e-3) / 1e9)
+    return best
+
+
+def cpu_baseline(sp, inputs, B, budget_s):
+    """The oracle, as it is, on host cores: one request's layer-step (score,
+    select, record gather of the selected blocks, fp32 attention) per call,
+    repeated over the batch until about budget_s seconds; scaled to layer-steps/s."""
+    import oracle
+    digests = {}
+    for r in range(B):
+        lr = inputs[(0, r)]
+        digests[r] = oracle.digest(lr.K, sp.dtype, sp.bs)  # setup, not timed
+    done, t0 = 0, time.perf_counter()
+    while True:
+        lr = inputs[(0, done % B)]
+        S = oracle.score(lr.q, sp.dtype, digests[done % B])
+        sel = oracle.select(S, lr.rq.k)
+        for b in sel.tolist():
+            t_a, t_b = b * sp.bs, min((b + 1) * sp.bs, lr.rq.ctx)
+            oracle.records(lr.K[t_a:t_b], lr.V[t_a:t_b], sp.bs)
+        oracle.attend_f32(lr.q, lr.K, lr.V, sp.dtype, sp.bs, sel)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s and done >= 1:
+            break
+    per_req = el / done
+    return {"value": 1.0 / (per_req * B), "unit": "layer-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} request-steps of layer 0 ({el:.1f} s single-threaded), "
+                      f"scaled to a {B}-request layer-step",
+            "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by request with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sp = synth.spec(args.config, L=args.layers)
+    reqs = synth.request_draws(sp)
+    B = len(reqs)
+    layers = list(range(args.layers))
+    t0 = time.time()
+    inputs = {}
+    keep_cpu = not args.no_cpu_baseline
+    log(f"generating {len(layers)} layers x {B} requests of '{sp.name}'")
+    for l in layers:
+        for r, rq in enumerate(reqs):
+            inputs[(l, r)] = synth.gen_layer_request(sp, l, r, rq)
+    log(f"generated in {time.time() - t0:.1f} s; offloading")
+    engine = kv.KVOFF_ENGINE_DMA if args.engine == "dma" else kv.KVOFF_ENGINE_ZEROCOPY
+    host_kind = kv.KVOFF_HOST_NONCOHERENT if args.host_mem == "noncoherent" else kv.KVOFF_HOST_COHERENT
+    case = H.build_case(sp, inputs, layers, reqs, host_kind=host_kind, two_regions=False)
+    if not keep_cpu:
+        inputs.clear()
+    else:  # only layer 0 is needed for the CPU baseline
+        for k in [k for k in inputs if k[0] != 0]:
+            del inputs[k]
+    log(f"setup done in {time.time() - t0:.1f} s")
+
+    mode = kv.KVOFF_SOLOHEAD
+    bufs = H.make_buffers(case, mode)
+    topk = [rq.k for rq in reqs]
+    scale = 1.0 / math.sqrt(sp.d)
+    stream = torch.cuda.current_stream()
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+
+    def one_step(i, evs=None):
+        l = layers[i % len(layers)]
+        if evs:
+            evs[0].record(stream)
+        kv.kvoff_select(case.ctx, l, case.rids, case.q[l], case.digest[l], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        kv.kvoff_recall(case.ctx, l, case.rids, mode, bufs.sel_idx, bufs.sel_cnt, case.k_stride,
+                        None, None, 0, case.pool, case.n_slots, case.recall_base[0], bufs.table,
+                        engine, stream=stream)
+        if evs:
+            evs[2].record(stream)
+        kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[l], case.pool, bufs.table,
+                               bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale, bufs.out,
+                               bufs.ws, stream=stream)
+        if evs:
+            evs[3].record(stream)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+
+    # algorithmic bytes per layer-step
+    rec_bytes = kv.kvoff_record_bytes(case.ctx)
+    nb_tot = sum(rq.nb for rq in reqs)
+    K_tot = sum(min(rq.k, rq.nb) for rq in reqs)
+    score_bytes = nb_tot * sp.Hkv * sp.d * 4 + B * sp.Hq * sp.d * sp.es + nb_tot * 8
+    recall_bytes = K_tot * rec_bytes
+    ws_bytes = kv.kvoff_workspace_size(case.ctx, kv.KVOFF_CALL_SPARSE_DECODE, B, case.k_stride, mode)
+    attend_bytes = K_tot * rec_bytes + B * sp.Hq * sp.d * (sp.es + 4) + 2 * ws_bytes
+
+    recall_gbps = recall_bytes / (rec_ms * 1e-3) / 1e9
+    log("measuring link and HBM copy peaks")
+    copy_peak, probe_peak = link_peaks(case)
+    link_peak = max(copy_peak, probe_peak)
+    hbm_copy = hbm_copy_peak()
+    result = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 3),
+        "unit": "layer-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sp.dtype == synth.BF16 else "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{sp.name}: batch {B}, {sp.Hq}/{sp.Hkv} heads, head_dim {sp.d}, "
+                        f"context {reqs[0].ctx}, block {sp.bs}, top-{reqs[0].k}, "
+                        f"{len(layers)} rotating layers",
+            "engine": args.engine, "host_mem": args.host_mem,
+            "global_batch": B, "seq_len": reqs[0].ctx,
+        },
+        "roofline": {
+            "kernel": "gather_kernel (zero-copy recall)" if engine == 0 else "hipMemcpyAsync runs",
+            "bound": "pcie", "achieved": round(recall_gbps, 2), "peak": PCIE_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(recall_gbps / PCIE_PEAK_GBPS, 4), "traffic": None,
+            "algorithmic_bytes": recall_bytes, "avg_ms": round(rec_ms, 4),
+            "frac_of_measured_link_peak": round(recall_gbps / link_peak, 4),
+        },
+        "phases": {
+            "select": {"kernels": "score_kernel + topk_kernel", "avg_ms": round(sel_ms, 4),
+                       "algorithmic_bytes": score_bytes,
+                       "hbm_gbps": round(score_bytes / (sel_ms * 1e-3) / 1e9, 1),
+                       "frac_of_hbm_peak": round(score_bytes / (sel_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "recall": {"avg_ms": round(rec_ms, 4), "bytes": recall_bytes,
+                       "gbps": round(recall_gbps, 2)},
+            "attend": {"kernels": "attend_kernel + combine_kernel", "avg_ms": round(att_ms, 4),
+                       "algorithmic_bytes": attend_bytes,
+                       "hbm_gbps": round(attend_bytes / (att_ms * 1e-3) / 1e9, 1),
+                       "frac_of_hbm_peak": round(attend_bytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        },
+        "link_peak_gbps": {"pinned_memcpy_1GiB": round(copy_peak, 2),
+                           "zero_copy_probe": round(probe_peak, 2)},
+        "recall_frac_of_link_peak": round(recall_gbps / link_peak, 4),
+        "hbm_copy_gbps_measured": round(hbm_copy, 1),
+    }
+    if keep_cpu:
+        log("timing the oracle on host cores")
+        result["cpu_baseline"] = cpu_baseline(sp, inputs, B, args.cpu_seconds)
+    H.destroy(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -122,7 +122,7 @@ def test_headwise_and_pool_hits(mode, engine):
 @pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 2), (16, 16), (64, 4)])
 def test_group_sizes(Hq, Hkv):
     H.log(f"[groups] Hq {Hq} Hkv {Hkv}")
-    s = synth.spec(2, B=2, Hq=Hq, Hkv=Hkv, ctx=2000, k=12, hot=5)
+    s = synth.spec(2, B=2, Hq=Hq, Hkv=Hkv, ctx=2000, k=12, hot=5, headwise=Hkv > 1)
     c, sl = _case(s, [0])
     try:
         _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
@@ -135,7 +135,7 @@ def test_group_sizes(Hq, Hkv):
 def test_degenerate_sizes():
     """k >= nb (take every block), k = 1, one-token and one-block contexts."""
     H.log("[degenerate]")
-    s = synth.spec(2, B=4, ctx=100, k=1, hot=1)
+    s = synth.spec(2, B=4, ctx=100, k=1, hot=1, headwise=True)
     reqs = [synth.Request(ctx=1, nb=1, k=1), synth.Request(ctx=33, nb=2, k=5),
             synth.Request(ctx=100, nb=4, k=1), synth.Request(ctx=96, nb=3, k=3)]
     c, sl = _case(s, [0], reqs=reqs)
