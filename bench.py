@@ -34,6 +34,26 @@ import synth  # noqa: E402
 from tests import gpu_harness as H  # noqa: E402
 
 METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM GB/s"
+
+# Counter traffic of the dominant kernel (gather_kernel) per launch on this
+# workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
+# and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
+# the recall source it was taken with: reported as null once that changes.
+GATHER_PMC = {"workload": (2, 4), "fetch_kib": 65662.45, "write_kib": 131076.02,
+              "fetch_scale": 1.9999, "write_scale": 1.0,
+              "recall_src_sha256": "65c7a1f5a4e71b8e1ea8466ec3fb511af7ba534385b9889ad58a1689bebe0a30"}
+
+
+def gather_traffic_bytes(config, layers):
+    import hashlib
+    if (config, layers) != GATHER_PMC["workload"]:
+        return None
+    src = os.path.join(ROOT, "sparse_kv_cache_mean_amd", "csrc", "recall.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != GATHER_PMC["recall_src_sha256"]:
+            return None
+    return int(GATHER_PMC["fetch_kib"] * 1024 * GATHER_PMC["fetch_scale"] +
+               GATHER_PMC["write_kib"] * 1024 * GATHER_PMC["write_scale"])
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 PCIE_PEAK_GBPS = 64.0       # PCIe 5.0 x16, one direction, published
 
@@ -49,10 +69,16 @@ def parse():
     p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--layers", type=int, default=4)
-    p.add_argument("--engine", choices=["zerocopy", "dma"], default="zerocopy")
+    p.add_argument("--engine", choices=["zerocopy", "dma", "staged"], default="zerocopy")
     p.add_argument("--host-mem", choices=["coherent", "noncoherent"], default="coherent")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-overlap", action="store_true",
+                   help="skip the overlapped kvoff_step measurement (for clean kernel traces)")
+    p.add_argument("--report", choices=["fragmentation"], default=None,
+                   help="instead of the bench line: recall of the headwise-vs-SoloHead "
+                        "workload (per-KV-head vs shared block sets, 25%% pool hits) with "
+                        "both engines: transfers, mean transfer size, GB/s")
     return p.parse_args()
 
 
@@ -79,11 +105,28 @@ def link_peaks(case):
     best_probe = 0.0
     for _ in range(5):
         s.record()
-        kv.kvoff_probe_host_read(base, n, sink)
+        kv.kvoff_probe_read(base, n, sink)
         e.record()
         e.synchronize()
         best_probe = max(best_probe, n / (s.elapsed_time(e) * 1e-3) / 1e9)
     return best_copy, best_probe
+
+
+def hbm_read_peak():
+    """Best of 5 reads of a 2 GiB device buffer with the probe kernel."""
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for wg in (2048, 4096, 8192):
+        for _ in range(3):
+            s.record()
+            kv.kvoff_probe_read(a, n, sink, wg)
+            e.record()
+            e.synchronize()
+            best = max(best, n / (s.elapsed_time(e) * 1e-3) / 1e9)
+    return best
 
 
 def hbm_copy_peak():
@@ -130,6 +173,52 @@ def cpu_baseline(sp, inputs, B, budget_s):
             "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
 
 
+def fragmentation_report(args):
+    """Recall of the headwise-vs-SoloHead workload: each selection mode with
+    each engine; transfers, mean transfer size and recall GB/s (wall clock
+    around the call, stream synchronised before and after)."""
+    sp = synth.spec(5)
+    reqs = synth.request_draws(sp)
+    inputs = {(0, r): synth.gen_layer_request(sp, 0, r, rq) for r, rq in enumerate(reqs)}
+    case = H.build_case(sp, inputs, [0], reqs, with_pool_hits=True, two_regions=False)
+    inputs.clear()
+    topk = [rq.k for rq in reqs]
+    out = {"workload": f"{sp.name}: batch {len(reqs)}, {sp.Hq}/{sp.Hkv} heads, context "
+                       f"{reqs[0].ctx}, block {sp.bs}, top-{reqs[0].k} shared or per KV head, "
+                       f"{int(sp.pool_frac * 100)}% of blocks resident in the HBM pool",
+           "runs": []}
+    for mode, mname in ((kv.KVOFF_SOLOHEAD, "solohead"), (kv.KVOFF_HEADWISE, "headwise")):
+        bufs = H.make_buffers(case, mode)
+        kv.kvoff_select(case.ctx, 0, case.rids, case.q[0], case.digest[0], case.nb_max, topk,
+                        mode, bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+        for engine, ename in ((kv.KVOFF_ENGINE_ZEROCOPY, "zerocopy"), (kv.KVOFF_ENGINE_DMA, "dma"),
+                              (kv.KVOFF_ENGINE_STAGED, "staged")):
+            def rec(stats=False):
+                return kv.kvoff_recall(case.ctx, 0, case.rids, mode, bufs.sel_idx, bufs.sel_cnt,
+                                       case.k_stride, case.pool_hit[0], case.pool_slot[0],
+                                       case.nb_max, case.pool, case.n_slots, case.recall_base[0],
+                                       bufs.table, engine, want_stats=stats)
+            st = rec(True)
+            for _ in range(3):
+                rec()
+            torch.cuda.synchronize()
+            n = 20
+            t = time.perf_counter()
+            for _ in range(n):
+                rec()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t) * 1e3 / n
+            out["runs"].append({
+                "mode": mname, "engine": ename, "ms": round(ms, 4),
+                "gbps": round(st["bytes"] / (ms * 1e-3) / 1e9, 2),
+                "transfers": st["transfers"], "items": st["items_recalled"],
+                "pool_hits": st["pool_hits"], "bytes": st["bytes"],
+                "mean_transfer_kib": round(st["bytes"] / max(1, st["transfers"]) / 1024, 2)})
+            log(str(out["runs"][-1]))
+    H.destroy(case)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -139,6 +228,8 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.report == "fragmentation":
+        return fragmentation_report(args)
     sp = synth.spec(args.config, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)
@@ -151,9 +242,10 @@ def main():
         for r, rq in enumerate(reqs):
             inputs[(l, r)] = synth.gen_layer_request(sp, l, r, rq)
     log(f"generated in {time.time() - t0:.1f} s; offloading")
-    engine = kv.KVOFF_ENGINE_DMA if args.engine == "dma" else kv.KVOFF_ENGINE_ZEROCOPY
+    engine = {"zerocopy": kv.KVOFF_ENGINE_ZEROCOPY, "dma": kv.KVOFF_ENGINE_DMA,
+              "staged": kv.KVOFF_ENGINE_STAGED}[args.engine]
     host_kind = kv.KVOFF_HOST_NONCOHERENT if args.host_mem == "noncoherent" else kv.KVOFF_HOST_COHERENT
-    case = H.build_case(sp, inputs, layers, reqs, host_kind=host_kind, two_regions=False)
+    case = H.build_case(sp, inputs, layers, reqs, host_kind=host_kind, two_regions=True)
     if not keep_cpu:
         inputs.clear()
     else:  # only layer 0 is needed for the CPU baseline
@@ -202,6 +294,32 @@ def main():
     rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
 
+    # the same layers through kvoff_step: recall of layer l+1 on a copy
+    # stream overlapped with select/attention of layer l on the compute stream
+    sets = [bufs, H.make_buffers(case, mode)]
+    outs = [torch.empty_like(bufs.out) for _ in layers]
+    copy = torch.cuda.Stream()
+
+    def step_all():
+        kv.kvoff_step(case.ctx, layer_begin=0, layer_end=len(layers), req_ids=case.rids,
+                      topk=topk, mode=mode, engine=engine, k_stride=case.k_stride,
+                      q=[case.q[l] for l in layers], digest=[case.digest[l] for l in layers],
+                      digest_stride=case.nb_max, slot_pool=case.pool, n_slots=case.n_slots,
+                      recall_base_slot=case.recall_base, scores=[b.scores for b in sets],
+                      sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
+                      block_table=[b.table for b in sets], scale=scale, out=outs, ws=bufs.ws,
+                      compute_stream=stream, copy_stream=copy)
+
+    n_over = 0 if args.no_overlap else max(2, args.steps // len(layers))
+    for _ in range(2 if n_over else 0):
+        step_all()
+    torch.cuda.synchronize()
+    t_o = time.perf_counter()
+    for _ in range(n_over):
+        step_all()
+    torch.cuda.synchronize()
+    over_ms_per_layer = (time.perf_counter() - t_o) * 1e3 / max(1, n_over * len(layers))
+
     # algorithmic bytes per layer-step
     rec_bytes = kv.kvoff_record_bytes(case.ctx)
     nb_tot = sum(rq.nb for rq in reqs)
@@ -216,6 +334,7 @@ def main():
     copy_peak, probe_peak = link_peaks(case)
     link_peak = max(copy_peak, probe_peak)
     hbm_copy = hbm_copy_peak()
+    hbm_read = hbm_read_peak()
     result = {
         "metric": METRIC,
         "value": round(1e3 / ms_per_step, 3),
@@ -237,9 +356,14 @@ def main():
             "global_batch": B, "seq_len": reqs[0].ctx,
         },
         "roofline": {
-            "kernel": "gather_kernel (zero-copy recall)" if engine == 0 else "hipMemcpyAsync runs",
+            "kernel": {0: "gather_kernel (zero-copy recall)", 1: "hipMemcpyAsync per run",
+                       2: "CPU gather + bulk hipMemcpyAsync"}[engine],
             "bound": "pcie", "achieved": round(recall_gbps, 2), "peak": PCIE_PEAK_GBPS,
-            "unit": "GB/s", "frac": round(recall_gbps / PCIE_PEAK_GBPS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(recall_gbps / PCIE_PEAK_GBPS, 4),
+            "traffic": gather_traffic_bytes(args.config, args.layers)
+            if engine == kv.KVOFF_ENGINE_ZEROCOPY else None,
+            "traffic_note": "counter bytes per launch: host-link fetches + HBM writes "
+                            "(a copy moves each byte twice)",
             "algorithmic_bytes": recall_bytes, "avg_ms": round(rec_ms, 4),
             "frac_of_measured_link_peak": round(recall_gbps / link_peak, 4),
         },
@@ -255,10 +379,15 @@ def main():
                        "hbm_gbps": round(attend_bytes / (att_ms * 1e-3) / 1e9, 1),
                        "frac_of_hbm_peak": round(attend_bytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         },
+        "overlapped": None if args.no_overlap else {"layer_steps_per_s": round(1e3 / over_ms_per_layer, 3),
+                       "ms_per_layer": round(over_ms_per_layer, 4),
+                       "how": f"kvoff_step over the {len(layers)} layers, recall of layer l+1 "
+                              "on a second stream under select/attention of layer l"},
         "link_peak_gbps": {"pinned_memcpy_1GiB": round(copy_peak, 2),
                            "zero_copy_probe": round(probe_peak, 2)},
         "recall_frac_of_link_peak": round(recall_gbps / link_peak, 4),
         "hbm_copy_gbps_measured": round(hbm_copy, 1),
+        "hbm_read_gbps_measured": round(hbm_read, 1),
     }
     if keep_cpu:
         log("timing the oracle on host cores")

@@ -68,8 +68,15 @@ enum { KVOFF_F16 = 1, KVOFF_BF16 = 2 };
 
 /* selection modes */
 enum {
-  KVOFF_SOLOHEAD = 0, /* one block set per request, shared by all heads     */
-  KVOFF_HEADWISE = 1  /* one block set per KV head (fragmentation baseline) */
+  KVOFF_SOLOHEAD = 0,  /* one block set per request, shared by all heads     */
+  KVOFF_HEADWISE = 1,  /* one block set per KV head (fragmentation baseline) */
+  /* one shared set ranked by the guide's consensus rule ("SoloHead Sparse
+     Selection", consensus equation, applied across KV heads as in its
+     simulator's SoloHeadSelector): S[b] = max_g S_g[b] + lambda * mean_g
+     S_g[b], S_g the per-KV-head score; lambda per context (default 0.5).
+     Its selection, recall and attention use the SoloHead layouts, and
+     kvoff_recall / kvoff_sparse_decode treat it as KVOFF_SOLOHEAD. */
+  KVOFF_CONSENSUS = 2
 };
 
 /* recall engines */
@@ -80,7 +87,17 @@ enum {
   /* the selection is copied to the host, which issues one hipMemcpyAsync per
      coalesced run (per (block, KV head) slice in headwise mode) on the
      stream; synchronises that stream first */
-  KVOFF_ENGINE_DMA = 1
+  KVOFF_ENGINE_DMA = 1,
+  /* the guide's three-phase engine ("The Gather-Scatter I/O Engine"): host
+     worker threads gather the selected records into a pinned staging
+     buffer, which bulk hipMemcpyAsync copies (4 MiB chunks, issued as they
+     fill) move to HBM.  Items are placed compactly: the n-th recalled item
+     of the call (in request, [KV head,] rank order) goes to slot
+     recall_base_slot + n (headwise: slice recall_base_slot*Hkv + n); the
+     block table says where.  Synchronises the stream first; the staging
+     buffer (pinned, grown on demand) is reused once the previous call's
+     copies completed. */
+  KVOFF_ENGINE_STAGED = 2
 };
 
 /* kind of pinned host memory for the store */
@@ -130,6 +147,10 @@ int kvoff_destroy(kvoff_ctx* ctx);
 
 /* Bytes of one block record: 2 * Hkv * bs * d * es. */
 int64_t kvoff_record_bytes(const kvoff_ctx* ctx);
+
+/* Sets lambda of KVOFF_CONSENSUS (>= 0; the guide prints 0.5 in its formula
+ * and simulator and 1 in its worked figure).  Errors: EINVAL. */
+int kvoff_set_consensus_lambda(kvoff_ctx* ctx, double lambda);
 
 /* Reserves store capacity for a request of n_tokens tokens in every layer
  * (nb = ceil(n_tokens / bs) records per layer) and returns its id in
@@ -272,12 +293,13 @@ int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* args);
 
 /* ------------------------------------------------------------- diagnostics */
 
-/* Reads n_bytes (a multiple of 4096) of host memory at host_ptr (pinned,
- * from hipHostMalloc) with a GPU kernel over the host link and writes a
- * reduction to dev_sink (>= 4096 bytes): a probe of the link's read rate for
- * the zero-copy engine.  n_wg workgroups (0 = default). */
-int kvoff_probe_host_read(const void* host_ptr, int64_t n_bytes, void* dev_sink, int32_t n_wg,
-                          void* stream);
+/* Reads n_bytes (a multiple of 4096) at ptr with a GPU kernel and writes an
+ * XOR reduction to dev_sink (>= 4096 bytes).  ptr is device memory or pinned
+ * host memory from hipHostMalloc (read over the host link through its mapped
+ * address): a probe of the achievable read rate for the recall kernel (host)
+ * and of HBM (device).  n_wg workgroups (0 = default). */
+int kvoff_probe_read(const void* ptr, int64_t n_bytes, void* dev_sink, int32_t n_wg,
+                     void* stream);
 
 const char* kvoff_strerror(int status);
 const char* kvoff_last_error(void);

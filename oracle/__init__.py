@@ -51,6 +51,7 @@ def lib():
         L.oracle_digest.argtypes = [vp, ci, i64, ci, ci, ci, vp]
         L.oracle_score.argtypes = [vp, ci, ci, ci, ci, vp, i64, vp]
         L.oracle_score_headwise.argtypes = [vp, ci, ci, ci, ci, vp, i64, vp]
+        L.oracle_score_consensus.argtypes = [vp, ci, ci, ci, ci, vp, i64, ctypes.c_double, vp]
         L.oracle_select.argtypes = [vp, i64, i64, vp]
         L.oracle_select.restype = i64
         L.oracle_records.argtypes = [vp, vp, i64, ci, ci, ci, vp]
@@ -116,6 +117,16 @@ def score_headwise(q: np.ndarray, dtype: int, D: np.ndarray) -> np.ndarray:
     nb, Hkv, _ = D.shape
     S = np.empty((Hkv, nb), np.float64)
     lib().oracle_score_headwise(_p(q), dtype, Hq, Hkv, d, _p(D), nb, _p(S))
+    return S
+
+
+def score_consensus(q: np.ndarray, dtype: int, D: np.ndarray, lam: float) -> np.ndarray:
+    q = _u16(q)
+    D = np.ascontiguousarray(D, dtype=np.float32)
+    Hq, d = q.shape
+    nb, Hkv, _ = D.shape
+    S = np.empty(nb, np.float64)
+    lib().oracle_score_consensus(_p(q), dtype, Hq, Hkv, d, _p(D), nb, lam, _p(S))
     return S
 
 

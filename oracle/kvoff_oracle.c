@@ -88,6 +88,21 @@ void oracle_score_headwise(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
   }
 }
 
+void oracle_score_consensus(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
+                            const float* D, int64_t nb, double lambda, double* S) {
+  double* Sg = (double*)malloc((size_t)Hkv * (size_t)nb * sizeof(double));
+  oracle_score_headwise(q, dtype, Hq, Hkv, d, D, nb, Sg);
+  for (int64_t b = 0; b < nb; ++b) {
+    double mx = Sg[b], sum = 0.0;
+    for (int g = 0; g < Hkv; ++g) {
+      if (Sg[g * nb + b] > mx) mx = Sg[g * nb + b];
+      sum += Sg[g * nb + b];
+    }
+    S[b] = mx + lambda * (sum / (double)Hkv);
+  }
+  free(Sg);
+}
+
 /* ---------------------------------------------------------------- select */
 
 typedef struct {

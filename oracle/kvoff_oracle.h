@@ -71,6 +71,14 @@ void oracle_score(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
 void oracle_score_headwise(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
                            const float* D, int64_t nb, double* S);
 
+/* Consensus score of every block, the guide's SoloHead consensus rule
+ * ("PulseInfer Guide", aiFetchly, section "SoloHead Sparse Selection",
+ * consensus equation; its simulator's SoloHeadSelector applies it across KV
+ * heads): S[b] = max_g S_g[b] + lambda * (sum_g S_g[b]) / Hkv, where S_g is
+ * the per-KV-head score of oracle_score_headwise.  S is [nb]. */
+void oracle_score_consensus(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
+                            const float* D, int64_t nb, double lambda, double* S);
+
 /* Top-k selection over nb scores: sel receives K = min(k, nb) block ids in
  * ascending order; returns K, or -1 if k < 1. */
 int64_t oracle_select(const double* S, int64_t nb, int64_t k, int32_t* sel);

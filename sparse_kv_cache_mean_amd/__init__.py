@@ -23,16 +23,17 @@ LIB_PATH = os.path.join(_HERE, "libkvoff.so")
 KVOFF_OK = 0
 KVOFF_EINVAL, KVOFF_ENOMEM, KVOFF_ENODEV, KVOFF_EHIP, KVOFF_ERANGE, KVOFF_ESTATE = range(-1, -7, -1)
 KVOFF_F16, KVOFF_BF16 = 1, 2
-KVOFF_SOLOHEAD, KVOFF_HEADWISE = 0, 1
-KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA = 0, 1
+KVOFF_SOLOHEAD, KVOFF_HEADWISE, KVOFF_CONSENSUS = 0, 1, 2
+KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA, KVOFF_ENGINE_STAGED = 0, 1, 2
 KVOFF_HOST_COHERENT, KVOFF_HOST_NONCOHERENT = 0, 1
 KVOFF_CALL_SPARSE_DECODE, KVOFF_CALL_STEP = 1, 2
 KVOFF_MAX_BATCH = 128
 
 EXPORTS = (
-    "kvoff_create", "kvoff_destroy", "kvoff_record_bytes", "kvoff_register_request",
+    "kvoff_create", "kvoff_destroy", "kvoff_record_bytes", "kvoff_set_consensus_lambda",
+    "kvoff_register_request",
     "kvoff_host_record", "kvoff_offload_blocks", "kvoff_select", "kvoff_recall",
-    "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_host_read",
+    "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_read",
     "kvoff_strerror", "kvoff_last_error",
 )
 
@@ -100,6 +101,7 @@ def lib() -> ctypes.CDLL:
     L.kvoff_record_bytes.argtypes = [_vp]
     L.kvoff_record_bytes.restype = i64
     L.kvoff_register_request.argtypes = [_vp, i64, P(i32)]
+    L.kvoff_set_consensus_lambda.argtypes = [_vp, ctypes.c_double]
     L.kvoff_host_record.argtypes = [_vp, i32, i32, i64, P(_vp)]
     L.kvoff_offload_blocks.argtypes = [_vp, i32, i32, _vp, _vp, _vp, _vp]
     L.kvoff_select.argtypes = [_vp, i32, i32, _vp, _vp, _vp, i64, _vp, i32, _vp, _vp, _vp, i32, _vp]
@@ -110,14 +112,15 @@ def lib() -> ctypes.CDLL:
     L.kvoff_workspace_size.argtypes = [_vp, i32, i32, i32, i32]
     L.kvoff_workspace_size.restype = sz
     L.kvoff_step.argtypes = [_vp, P(kvoff_step_args)]
-    L.kvoff_probe_host_read.argtypes = [_vp, i64, _vp, i32, _vp]
+    L.kvoff_probe_read.argtypes = [_vp, i64, _vp, i32, _vp]
     L.kvoff_strerror.argtypes = [ctypes.c_int]
     L.kvoff_strerror.restype = ctypes.c_char_p
     L.kvoff_last_error.argtypes = []
     L.kvoff_last_error.restype = ctypes.c_char_p
     for name in ("kvoff_create", "kvoff_destroy", "kvoff_register_request", "kvoff_host_record",
+                 "kvoff_set_consensus_lambda",
                  "kvoff_offload_blocks", "kvoff_select", "kvoff_recall", "kvoff_sparse_decode",
-                 "kvoff_step", "kvoff_probe_host_read"):
+                 "kvoff_step", "kvoff_probe_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -173,6 +176,10 @@ def kvoff_destroy(ctx: int) -> None:
 
 def kvoff_record_bytes(ctx: int) -> int:
     return int(lib().kvoff_record_bytes(ctx))
+
+
+def kvoff_set_consensus_lambda(ctx: int, lam: float) -> None:
+    _check(lib().kvoff_set_consensus_lambda(ctx, lam))
 
 
 def kvoff_register_request(ctx: int, n_tokens: int) -> int:
@@ -275,5 +282,5 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
     return st.as_dict() if st is not None else None
 
 
-def kvoff_probe_host_read(host_ptr: int, n_bytes: int, sink, n_wg: int = 0, stream=None) -> None:
-    _check(lib().kvoff_probe_host_read(host_ptr, n_bytes, _ptr(sink), n_wg, _stream(stream)))
+def kvoff_probe_read(ptr, n_bytes: int, sink, n_wg: int = 0, stream=None) -> None:
+    _check(lib().kvoff_probe_read(_ptr(ptr), n_bytes, _ptr(sink), n_wg, _stream(stream)))

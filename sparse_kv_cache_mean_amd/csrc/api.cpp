@@ -125,6 +125,7 @@ int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
     ctx->store_dev = (uint8_t*)dp;
     e = hipMalloc(&ctx->d_reqs, sizeof(ReqDev) * (size_t)c.max_requests);
     if (e == hipSuccess) e = hipMalloc(&ctx->d_counters, 8 * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_stage, hipEventDisableTiming);
     for (int i = 0; i < 2 && e == hipSuccess; ++i) {
       e = hipEventCreateWithFlags(&ctx->ev_sel[i], hipEventDisableTiming);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_rec[i], hipEventDisableTiming);
@@ -153,6 +154,10 @@ int kvoff_destroy(kvoff_ctx* ctx) {
     if (ctx->ev_sel[i]) (void)hipEventDestroy(ctx->ev_sel[i]);
     if (ctx->ev_rec[i]) (void)hipEventDestroy(ctx->ev_rec[i]);
   }
+  stage_pool_destroy(ctx);
+  if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
+  if (ctx->stage_buf) (void)hipHostFree(ctx->stage_buf);
+  if (ctx->table_host) (void)hipHostFree(ctx->table_host);
   if (ctx->d_counters) (void)hipFree(ctx->d_counters);
   if (ctx->d_reqs) (void)hipFree(ctx->d_reqs);
   if (ctx->store) (void)hipHostFree(ctx->store);
@@ -162,6 +167,13 @@ int kvoff_destroy(kvoff_ctx* ctx) {
 }
 
 int64_t kvoff_record_bytes(const kvoff_ctx* ctx) { return ctx ? ctx->rec_bytes : 0; }
+
+int kvoff_set_consensus_lambda(kvoff_ctx* ctx, double lambda) {
+  if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
+  if (!(lambda >= 0.0) || lambda > 1e6) return fail(KVOFF_EINVAL, "lambda %g outside [0, 1e6]", lambda);
+  ctx->consensus_lambda = lambda;
+  return KVOFF_OK;
+}
 
 int kvoff_register_request(kvoff_ctx* ctx, int64_t n_tokens, int32_t* req_id) {
   if (!ctx || !req_id) return fail(KVOFF_EINVAL, "ctx and req_id must be non-NULL");
@@ -235,7 +247,8 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
     return fail(KVOFF_ERANGE, "layer %d outside [0, %d)", layer, ctx->cfg.num_layers);
   if (!q_dev || !digest_dev || !topk || !scores_dev || !sel_idx_dev || !sel_cnt_dev)
     return fail(KVOFF_EINVAL, "NULL buffer argument");
-  if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE) return fail(KVOFF_EINVAL, "mode %d", mode);
+  if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE && mode != KVOFF_CONSENSUS)
+    return fail(KVOFF_EINVAL, "mode %d", mode);
   if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
   int64_t max_nb = 0;
   for (int i = 0; i < n_req; ++i) {
@@ -253,7 +266,9 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
   hipStream_t s = (hipStream_t)stream;
   st = launch_score(ctx, b, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
   if (st) return st;
-  return launch_topk(ctx, b, topk, mode, scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
+  // a consensus selection is one shared set, laid out like SoloHead's
+  const int32_t sel_mode = mode == KVOFF_HEADWISE ? KVOFF_HEADWISE : KVOFF_SOLOHEAD;
+  return launch_topk(ctx, b, topk, sel_mode, scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
                      k_stride, s);
 }
 
@@ -280,6 +295,7 @@ static int recall_impl(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, i
                 (long long)a.recall_base_slot,
                 (long long)(a.recall_base_slot + (int64_t)b.n * a.k_stride), (long long)n_slots);
   if (engine == KVOFF_ENGINE_DMA) return recall_dma(ctx, b, a, stats, s);
+  if (engine == KVOFF_ENGINE_STAGED) return recall_staged(ctx, b, a, stats, s);
   if (engine != KVOFF_ENGINE_ZEROCOPY) return fail(KVOFF_EINVAL, "engine %d", engine);
   int st;
   if (stats && (st = launch_zero_counters(ctx, s))) return st;
@@ -303,6 +319,7 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
   if ((st = check_layer_offloaded(ctx, layer, b))) return st;
   if (!sel_idx_dev || !sel_cnt_dev || !slot_pool_dev || !block_table_dev)
     return fail(KVOFF_EINVAL, "NULL buffer argument");
+  if (mode == KVOFF_CONSENSUS) mode = KVOFF_SOLOHEAD;  // one shared set
   if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE) return fail(KVOFF_EINVAL, "mode %d", mode);
   if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
   if ((pool_hit_dev == nullptr) != (pool_slot_dev == nullptr))
@@ -339,6 +356,7 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
   if (n_req == 0) return KVOFF_OK;
   if (!q_dev || !slot_pool_dev || !block_table_dev || !sel_idx_dev || !sel_cnt_dev || !out_dev)
     return fail(KVOFF_EINVAL, "NULL buffer argument");
+  if (mode == KVOFF_CONSENSUS) mode = KVOFF_SOLOHEAD;  // one shared set
   if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE) return fail(KVOFF_EINVAL, "mode %d", mode);
   if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
   size_t need = attend_ws_bytes(ctx, n_req, k_stride);
@@ -349,12 +367,20 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
                        sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
 }
 
-int kvoff_probe_host_read(const void* host_ptr, int64_t n_bytes, void* dev_sink, int32_t n_wg,
-                          void* stream) {
-  if (!host_ptr || !dev_sink) return fail(KVOFF_EINVAL, "NULL pointer");
+int kvoff_probe_read(const void* ptr, int64_t n_bytes, void* dev_sink, int32_t n_wg,
+                     void* stream) {
+  if (!ptr || !dev_sink) return fail(KVOFF_EINVAL, "NULL pointer");
   if (n_bytes <= 0 || n_bytes % 4096) return fail(KVOFF_EINVAL, "n_bytes must be a positive multiple of 4096");
-  void* dp = nullptr;
-  KVOFF_HIP(hipHostGetDevicePointer(&dp, const_cast<void*>(host_ptr), 0));
+  hipPointerAttribute_t attr;
+  KVOFF_HIP(hipPointerGetAttributes(&attr, ptr));
+  const void* dp = ptr;
+  if (attr.type == hipMemoryTypeHost) {
+    void* mapped = nullptr;
+    KVOFF_HIP(hipHostGetDevicePointer(&mapped, const_cast<void*>(ptr), 0));
+    dp = mapped;
+  } else if (attr.type != hipMemoryTypeDevice) {
+    return fail(KVOFF_EINVAL, "probe pointer is neither device memory nor pinned host memory");
+  }
   return launch_probe(dp, n_bytes, dev_sink, n_wg, (hipStream_t)stream);
 }
 

@@ -21,8 +21,12 @@
 //   PV   fp32 VALU: lane (token group quad, dim group col) loads 16 bytes of
 //        V rows t = quad + 4k and accumulates o[h][8 dims] for all G heads.
 // The four waves merge in LDS; one partial (m, l, o[128]) per (head, split)
-// goes to the workspace and combine_kernel merges splits in fixed order, so
-// results are deterministic.
+// goes to the workspace and combine_kernel merges the splits in fixed split
+// order, so results are deterministic.  (Merging in the last-arriving
+// workgroup instead needs a device-scope release per workgroup, which on this
+// part writes back the L2 that the recall just filled; measured 8x slower.)
+#include <cstdlib>
+
 #include "kvoff_internal.h"
 
 namespace kvoff {
@@ -106,10 +110,21 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   // B fragments: query head g*G + col, dims m*32 + quad*8 .. +7
   uint4 qf[4];
   {
-    const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + col) * D;
+    const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + min(col, G - 1)) * D;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      qf[m] = col < G ? *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8) : make_uint4(0, 0, 0, 0);
+    for (int m = 0; m < 4; ++m) {
+      qf[m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
+      if (col >= G) qf[m] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  // the wave's block ids and table entries, loaded once (at most 4 blocks)
+  int blk_w[4];
+  int64_t ent_w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = min(i0 + k, max(i1 - 1, 0));
+    blk_w[k] = a.sel_idx[row + i];
+    ent_w[k] = a.table[row + i];
   }
 
   float m_run = -INFINITY, l_run = 0.f;  // head col's running max (log2) and sum
@@ -119,9 +134,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
 
-  for (int i = i0; i < i1; ++i) {
-    const int blk = a.sel_idx[row + i];
-    const int64_t ent = a.table[row + i];
+#pragma unroll 1
+  for (int k = 0; k < 4; ++k) {
+    if (i0 + k >= i1) break;
+    const int blk = blk_w[k];
+    const int64_t ent = ent_w[k];
     const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
     const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
     const uint16_t* Vp = Kp + BS * D;
@@ -237,25 +254,55 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     }
     P[2 + j] = O;
   }
+
 }
 
+// blocks per wave (at most 4: the per-wave index cache)
+// One workgroup per (request, head), one thread per dim: single-pass merge
+// of the splits in order, loads batched 8 splits at a time.
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, float* out, int S) {
   const int64_t rh = blockIdx.x;  // request * Hq + head
   const int j = threadIdx.x;
   const float* P = part + rh * S * PART;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, P[s * PART]);
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float m = P[s * PART];
-    const float f = m == -INFINITY ? 0.f : exp2f(m - M);
-    L = fmaf(P[s * PART + 1], f, L);
-    O = fmaf(P[s * PART + 2 + j], f, O);
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float m[8], l[8], o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int t = min(s0 + k, S - 1);
+      m[k] = P[t * PART];
+      l[k] = P[t * PART + 1];
+      o[k] = P[t * PART + 2 + j];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k >= S || m[k] == -INFINITY) continue;
+      if (m[k] > M) {
+        const float f = M == -INFINITY ? 0.f : exp2f(M - m[k]);
+        L = fmaf(L, f, l[k]);
+        O = fmaf(O, f, o[k]);
+        M = m[k];
+      } else {
+        const float f = exp2f(m[k] - M);
+        L = fmaf(l[k], f, L);
+        O = fmaf(o[k], f, O);
+      }
+    }
   }
   out[rh * kHeadDim + j] = L > 0.f ? O / L : 0.f;
 }
 
-int attend_bpw(int32_t k_stride) { return k_stride <= 128 ? 2 : 4; }
+// blocks per wave (at most 4: the per-wave index cache); KVOFF_ATT_BPW
+// overrides the default for tuning sweeps
+int attend_bpw(int32_t k_stride) {
+  static const int forced = [] {
+    const char* e = std::getenv("KVOFF_ATT_BPW");
+    const int v = e ? std::atoi(e) : 0;
+    return v >= 1 && v <= 4 ? v : 0;
+  }();
+  if (forced) return forced;
+  return k_stride <= 128 ? 2 : 4;
+}
 
 template <int G, int BS>
 void launch_g_bs(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s) {

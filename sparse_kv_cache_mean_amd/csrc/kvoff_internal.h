@@ -35,12 +35,15 @@ struct ReqHost {
   int64_t nb;
 };
 
+class StagePool;
+
 }  // namespace kvoff
 
 struct kvoff_ctx {
   kvoff_config cfg;
   int device = 0;
   int G = 1;
+  double consensus_lambda = 0.5;  // KVOFF_CONSENSUS mode
   int64_t rec_bytes = 0;    // 2 * Hkv * bs * d * es
   int64_t slice_bytes = 0;  // 2 * bs * d * es (K and V of one KV head)
   uint8_t* store = nullptr; // pinned host store (mapped into the GPU's address space)
@@ -52,6 +55,14 @@ struct kvoff_ctx {
   unsigned long long* d_counters = nullptr;  // recall statistics (device)
   hipEvent_t ev_sel[2] = {nullptr, nullptr};
   hipEvent_t ev_rec[2] = {nullptr, nullptr};
+  // staged (CPU gather + bulk copy) recall engine
+  kvoff::StagePool* stage_pool = nullptr;  // host worker threads, created on first use
+  void* stage_buf = nullptr;                // pinned staging buffer, grown on demand
+  size_t stage_cap = 0;
+  void* table_host = nullptr;               // pinned block-table staging
+  size_t table_cap = 0;
+  hipEvent_t ev_stage = nullptr;            // behind the last staged copy
+  bool ev_stage_pending = false;
 };
 
 namespace kvoff {
@@ -107,6 +118,9 @@ int launch_zero_counters(const kvoff_ctx* ctx, hipStream_t stream);
 
 int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, kvoff_stats* stats,
                hipStream_t stream);
+int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, kvoff_stats* stats,
+                  hipStream_t stream);
+void stage_pool_destroy(kvoff_ctx* ctx);
 
 // split policy of the attention kernel: number of splits per (request, KV head)
 int attend_splits(int32_t k_stride);

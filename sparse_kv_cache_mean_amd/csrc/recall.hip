@@ -164,7 +164,7 @@ int gather_grid_cap() {
   static int cap = [] {
     const char* e = std::getenv("KVOFF_GATHER_WG");
     int v = e ? std::atoi(e) : 0;
-    return v > 0 ? v : 2048;
+    return v > 0 ? v : 128;  // measured: 32..256 saturate the link, more congest it
   }();
   return cap;
 }

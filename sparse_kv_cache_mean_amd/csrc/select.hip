@@ -20,13 +20,23 @@
 // of the fp64 scores (8 passes of 8 bits, LDS histogram), then an ordered
 // compaction in block order that keeps every key above the threshold and the
 // lowest-numbered keys equal to it.  Output is ascending block ids.
+#include <algorithm>
+#include <cstdlib>
+
 #include "kvoff_internal.h"
 
 namespace kvoff {
 namespace {
 
-constexpr int SCORE_BPW = 4;
-constexpr int SCORE_WG_BLOCKS = 4 * SCORE_BPW;
+// blocks per wave of score_kernel (digest rows in flight per lane: BPW * NC)
+int score_bpw() {
+  static const int v = [] {
+    const char* e = std::getenv("KVOFF_SCORE_BPW");
+    const int x = e ? std::atoi(e) : 0;
+    return x == 2 || x == 4 || x == 8 ? x : 4;
+  }();
+  return v;
+}
 
 struct ScoreArgs {
   BatchIds batch;
@@ -36,58 +46,93 @@ struct ScoreArgs {
   double* scores;
   int64_t stride;
   int32_t Hq, Hkv, G, bf16;
+  double lambda;  // consensus mode only
 };
 
-__device__ __forceinline__ double widen(uint16_t h, int bf16) {
-  if (bf16) return (double)__uint_as_float((uint32_t)h << 16);
-  return (double)__builtin_bit_cast(_Float16, h);
+enum { MODE_SOLO = 0, MODE_HEADWISE = 1, MODE_CONSENSUS = 2 };
+
+template <bool BF16>
+__device__ __forceinline__ double widen_t(uint16_t h) {
+  if constexpr (BF16) return (double)__uint_as_float((uint32_t)h << 16);
+  else return (double)__builtin_bit_cast(_Float16, h);
 }
 
-template <int NC, bool HW>
+template <int NC, int MODE, bool BF16, int SCORE_BPW>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  constexpr int SCORE_WG_BLOCKS = 4 * SCORE_BPW;
   __shared__ double u_s[NC * 256];
+  extern __shared__ uint4 q_s[];  // the request's q rows, Hq * 16 chunks of 16 bytes
   const int r = blockIdx.y;
   const ReqDev rq = a.reqs[a.batch.id[r]];
   const int64_t b0 = (int64_t)blockIdx.x * SCORE_WG_BLOCKS;
   if (b0 >= rq.nb) return;  // uniform over the workgroup
   const int F = a.Hkv * kHeadDim;
+  const int tid = threadIdx.x;
 
-  const uint16_t* qr = a.q + (int64_t)r * a.Hq * kHeadDim;
-  for (int idx = threadIdx.x; idx < NC * 256; idx += 256) {
-    double s = 0.0;
-    if (idx < F) {
-      const int g = idx / kHeadDim, j = idx % kHeadDim;
-      for (int i = 0; i < a.G; ++i) s += widen(qr[(g * a.G + i) * kHeadDim + j], a.bf16);
+  // Load order: the digests first, then the request's q rows.  Loads retire
+  // in issue order, so waiting for the q rows waits for the digests too:
+  // one memory round trip covers both, and the q -> u_g preamble runs while
+  // nothing else is outstanding.
+  // Every load is unconditional (block index clamped to the last block,
+  // column clamped inside the row) so all of them are in flight together;
+  // results of clamped blocks are not stored, clamped columns meet u = 0.
+  const float* dr = a.digest + (int64_t)r * a.stride * F;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t bw = b0 + wave * SCORE_BPW;
+  float4 v[SCORE_BPW][NC];
+#pragma unroll
+  for (int k = 0; k < SCORE_BPW; ++k) {
+    const int64_t b = min<int64_t>(bw + k, rq.nb - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int idx = min(c * 256 + lane * 4, F - 4);
+      v[k][c] = *reinterpret_cast<const float4*>(dr + b * F + idx);
     }
-    u_s[idx] = s;
+  }
+  // q rows: 4 chunks of 16 bytes per thread (Hq <= 64 in one round); the
+  // LDS copy has room for all 4, so stores are unconditional too
+  const uint4* qr = reinterpret_cast<const uint4*>(a.q + (int64_t)r * a.Hq * kHeadDim);
+  const int nq = a.Hq * (kHeadDim / 8);
+  uint4 qw[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qw[c] = qr[min(c * 256 + tid, nq - 1)];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) q_s[c * 256 + tid] = qw[c];
+  for (int i = 4 * 256 + tid; i < nq; i += 256) q_s[i] = qr[i];  // Hq > 64 only
+  __syncthreads();
+
+  // u_g = sum of the group's G query heads, in fp64: thread (g, 8-dim group)
+  for (int t = tid; t < NC * 32; t += 256) {
+    const int g = t >> 4, dg = t & 15;
+    double s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0;
+    if (g < a.Hkv) {
+      for (int i = 0; i < a.G; ++i) {
+        const uint4 w = q_s[(g * a.G + i) * (kHeadDim / 8) + dg];
+        const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[2 * e] += widen_t<BF16>((uint16_t)(x[e] & 0xffffu));
+          s[2 * e + 1] += widen_t<BF16>((uint16_t)(x[e] >> 16));
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u_s[t * 8 + e] = s[e];
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   double u[NC][4];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) u[c][e] = u_s[c * 256 + lane * 4 + e];
 
-  const float* dr = a.digest + (int64_t)r * a.stride * F;
-  const int64_t bw = b0 + wave * SCORE_BPW;
-  float4 v[SCORE_BPW][NC];
-#pragma unroll
-  for (int k = 0; k < SCORE_BPW; ++k)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int idx = c * 256 + lane * 4;
-      const int64_t b = bw + k;
-      v[k][c] = (b < rq.nb && idx < F)
-                    ? *reinterpret_cast<const float4*>(dr + b * F + idx)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
 #pragma unroll
   for (int k = 0; k < SCORE_BPW; ++k) {
     const int64_t b = bw + k;
-    if (!HW) {
+    if constexpr (MODE == MODE_SOLO) {
       double acc = 0.0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -100,6 +145,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
       if (lane == 0 && b < rq.nb) a.scores[(int64_t)r * a.stride + b] = acc;
     } else {
+      // per-KV-head sums: a KV head's 128 dims are 32 consecutive lanes of
+      // one chunk, so chunk c holds heads 2c (lanes 0-31) and 2c+1 (32-63)
+      double sg[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         double acc = 0.0;
@@ -107,12 +155,37 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         acc = fma(u[c][1], (double)v[k][c].y, acc);
         acc = fma(u[c][2], (double)v[k][c].z, acc);
         acc = fma(u[c][3], (double)v[k][c].w, acc);
-        // a KV head's 128 dims are 32 consecutive lanes of one chunk
 #pragma unroll
         for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        const int g = (c * 256 + lane * 4) / kHeadDim;
-        if ((lane & 31) == 0 && b < rq.nb && g < a.Hkv)
-          a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = acc;
+        sg[c] = acc;
+      }
+      if constexpr (MODE == MODE_HEADWISE) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int g = (c * 256 + lane * 4) / kHeadDim;
+          if ((lane & 31) == 0 && b < rq.nb && g < a.Hkv)
+            a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = sg[c];
+        }
+      } else {
+        // consensus: S = max_g S_g + lambda * mean_g S_g, heads in order
+        double hi[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) hi[c] = __shfl(sg[c], 32);
+        if (lane == 0 && b < rq.nb) {
+          double mx = sg[0], sum = 0.0;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            if (2 * c < a.Hkv) {
+              mx = fmax(mx, sg[c]);
+              sum += sg[c];
+            }
+            if (2 * c + 1 < a.Hkv) {
+              mx = fmax(mx, hi[c]);
+              sum += hi[c];
+            }
+          }
+          a.scores[(int64_t)r * a.stride + b] = mx + a.lambda * (sum / (double)a.Hkv);
+        }
       }
     }
   }
@@ -137,10 +210,12 @@ __device__ __forceinline__ uint64_t score_key(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-template <bool HW>
+// KPT > 0: each thread keeps the keys of blocks tid + 256*k (k < KPT) in
+// registers (nb <= 256*KPT); KPT == 0 re-reads the scores every pass.
+template <bool HW, int KPT>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t s_digit, s_above, s_count;
   __shared__ uint32_t w_take[4], w_eq[4];
 
   const int r = HW ? blockIdx.x / a.Hkv : blockIdx.x;
@@ -152,6 +227,17 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int nb = rq.nb;
   const int K = a.k[r] < nb ? a.k[r] : nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunks = (nb + 255) / 256;
+
+  uint64_t keys[KPT > 0 ? KPT : 1];
+  if constexpr (KPT > 0) {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) keys[k] = score_key(S[min(tid + 256 * k, nb - 1)]);
+  }
+  auto key_at = [&](int k) -> uint64_t {
+    if constexpr (KPT > 0) return keys[k];
+    else return score_key(S[min(tid + 256 * k, nb - 1)]);
+  };
 
   uint64_t prefix = 0, mask = 0;
   uint32_t need = (uint32_t)K;
@@ -159,9 +245,13 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     const int shift = 56 - 8 * pass;
     hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < nb; i += 256) {
-      const uint64_t key = score_key(S[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+#pragma unroll
+    for (int k = 0; k < (KPT > 0 ? KPT : 1); ++k) {
+      for (int kk = k; kk < (KPT > 0 ? k + 1 : chunks); ++kk) {
+        const uint64_t key = key_at(kk);
+        if (tid + 256 * kk < nb && (key & mask) == prefix)
+          atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -184,6 +274,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
         if (run < need && need <= run + c[e]) {
           s_digit = 255u - 4u * lane - e;
           s_above = run;
+          s_count = c[e];
         }
         run += c[e];
       }
@@ -192,52 +283,88 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     prefix |= (uint64_t)s_digit << shift;
     mask |= 255ull << shift;
     need -= s_above;
+    const bool whole_bucket = s_count == need;  // every key of the bucket is taken
     __syncthreads();
+    if (whole_bucket) break;
   }
-  const uint64_t T = prefix;  // the K-th largest key; take `need` of its copies
+  // selected: masked key above the prefix, or equal to it and among the
+  // `need` lowest block ids with that masked key
 
   uint32_t taken = 0, eq_seen = 0;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  for (int base = 0; base < nb; base += 256) {
-    const int i = base + tid;
-    const bool valid = i < nb;
-    const uint64_t key = valid ? score_key(S[i]) : 0;
-    const bool gt = valid && key > T;
-    const bool eq = valid && key == T;
-    const uint64_t eq_b = __ballot(eq);
-    if (lane == 0) w_eq[wave] = (uint32_t)__popcll(eq_b);
-    __syncthreads();
-    uint32_t eq_before = eq_seen + (uint32_t)__popcll(eq_b & lt_mask);
-    uint32_t eq_total = 0;
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) eq_before += w_eq[w];
-      eq_total += w_eq[w];
+#pragma unroll
+  for (int k = 0; k < (KPT > 0 ? KPT : 1); ++k) {
+    for (int kk = k; kk < (KPT > 0 ? k + 1 : chunks); ++kk) {
+      if (256 * kk >= nb) break;  // uniform
+      const int i = tid + 256 * kk;
+      const bool valid = i < nb;
+      const uint64_t mk = key_at(kk) & mask;
+      const bool gt = valid && mk > prefix;
+      const bool eq = valid && mk == prefix;
+      const uint64_t eq_b = __ballot(eq);
+      if (lane == 0) w_eq[wave] = (uint32_t)__popcll(eq_b);
+      __syncthreads();
+      uint32_t eq_before = eq_seen + (uint32_t)__popcll(eq_b & lt_mask);
+      uint32_t eq_total = 0;
+      for (int w = 0; w < 4; ++w) {
+        if (w < wave) eq_before += w_eq[w];
+        eq_total += w_eq[w];
+      }
+      const bool take = gt || (eq && eq_before < need);
+      const uint64_t tk_b = __ballot(take);
+      if (lane == 0) w_take[wave] = (uint32_t)__popcll(tk_b);
+      __syncthreads();
+      uint32_t pos = taken + (uint32_t)__popcll(tk_b & lt_mask);
+      uint32_t tk_total = 0;
+      for (int w = 0; w < 4; ++w) {
+        if (w < wave) pos += w_take[w];
+        tk_total += w_take[w];
+      }
+      if (take && pos < (uint32_t)K) out[pos] = i;  // pos < K by construction
+      taken += tk_total;
+      eq_seen += eq_total;
+      __syncthreads();
     }
-    const bool take = gt || (eq && eq_before < need);
-    const uint64_t tk_b = __ballot(take);
-    if (lane == 0) w_take[wave] = (uint32_t)__popcll(tk_b);
-    __syncthreads();
-    uint32_t pos = taken + (uint32_t)__popcll(tk_b & lt_mask);
-    uint32_t tk_total = 0;
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) pos += w_take[w];
-      tk_total += w_take[w];
-    }
-    if (take && pos < (uint32_t)K) out[pos] = i;  // pos < K by construction
-    taken += tk_total;
-    eq_seen += eq_total;
-    __syncthreads();
   }
   for (int i = K + tid; i < a.k_stride; i += 256) out[i] = -1;
   if (tid == 0 && g == 0) a.sel_cnt[r] = K;
 }
 
-template <int NC>
-void score_launch(const ScoreArgs& a, dim3 grid, bool hw, hipStream_t s) {
+template <int KPT>
+void topk_launch(const TopkArgs& a, dim3 grid, bool hw, hipStream_t s) {
   if (hw)
-    hipLaunchKernelGGL((score_kernel<NC, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<true, KPT>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((score_kernel<NC, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<false, KPT>), grid, dim3(256), 0, s, a);
+}
+
+template <int NC, int MODE, int BPW>
+void score_launch_b(const ScoreArgs& a, int64_t max_nb, hipStream_t s) {
+  const size_t lds = std::max<size_t>((size_t)a.Hq * kHeadDim * 2, 4 * 256 * 16);  // staged q rows
+  const dim3 grid((unsigned)((max_nb + 4 * BPW - 1) / (4 * BPW)), (unsigned)a.batch.n);
+  if (a.bf16)
+    hipLaunchKernelGGL((score_kernel<NC, MODE, true, BPW>), grid, dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((score_kernel<NC, MODE, false, BPW>), grid, dim3(256), lds, s, a);
+}
+
+template <int NC, int MODE>
+void score_launch_m(const ScoreArgs& a, int64_t max_nb, hipStream_t s) {
+  switch (score_bpw()) {
+    case 2: score_launch_b<NC, MODE, 2>(a, max_nb, s); break;
+    case 8: score_launch_b<NC, MODE, 8>(a, max_nb, s); break;
+    default: score_launch_b<NC, MODE, 4>(a, max_nb, s); break;
+  }
+}
+
+template <int NC>
+void score_launch(const ScoreArgs& a, int64_t max_nb, int mode, hipStream_t s) {
+  if (mode == KVOFF_HEADWISE)
+    score_launch_m<NC, MODE_HEADWISE>(a, max_nb, s);
+  else if (mode == KVOFF_CONSENSUS)
+    score_launch_m<NC, MODE_CONSENSUS>(a, max_nb, s);
+  else
+    score_launch_m<NC, MODE_SOLO>(a, max_nb, s);
 }
 
 }  // namespace
@@ -256,16 +383,15 @@ int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t max_nb, const 
   a.Hkv = ctx->cfg.num_kv_heads;
   a.G = ctx->G;
   a.bf16 = ctx->cfg.dtype == KVOFF_BF16;
+  a.lambda = ctx->consensus_lambda;
   const int F = a.Hkv * kHeadDim;
   const int NC = (F + 255) / 256;
-  dim3 grid((unsigned)((max_nb + SCORE_WG_BLOCKS - 1) / SCORE_WG_BLOCKS), (unsigned)b.n);
-  const bool hw = mode == KVOFF_HEADWISE;
   switch (NC) {
-    case 1: score_launch<1>(a, grid, hw, stream); break;
-    case 2: score_launch<2>(a, grid, hw, stream); break;
+    case 1: score_launch<1>(a, max_nb, mode, stream); break;
+    case 2: score_launch<2>(a, max_nb, mode, stream); break;
     case 3:
-    case 4: score_launch<4>(a, grid, hw, stream); break;
-    default: score_launch<8>(a, grid, hw, stream); break;
+    case 4: score_launch<4>(a, max_nb, mode, stream); break;
+    default: score_launch<8>(a, max_nb, mode, stream); break;
   }
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
@@ -284,10 +410,18 @@ int launch_topk(const kvoff_ctx* ctx, const BatchIds& b, const int32_t* topk_hos
   a.k_stride = k_stride;
   a.Hkv = ctx->cfg.num_kv_heads;
   for (int i = 0; i < KVOFF_MAX_BATCH; ++i) a.k[i] = i < b.n ? topk_host[i] : 0;
-  if (mode == KVOFF_HEADWISE)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)(b.n * a.Hkv)), dim3(256), 0, stream, a);
+  int64_t max_nb = 0;
+  for (int i = 0; i < b.n; ++i) max_nb = std::max<int64_t>(max_nb, ctx->reqs[b.id[i]].nb);
+  const bool hw = mode == KVOFF_HEADWISE;
+  const dim3 grid((unsigned)(hw ? b.n * a.Hkv : b.n));
+  if (max_nb <= 1024)
+    topk_launch<4>(a, grid, hw, stream);
+  else if (max_nb <= 4096)
+    topk_launch<16>(a, grid, hw, stream);
+  else if (max_nb <= 16384)
+    topk_launch<64>(a, grid, hw, stream);
   else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)b.n), dim3(256), 0, stream, a);
+    topk_launch<0>(a, grid, hw, stream);
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }

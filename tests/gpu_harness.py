@@ -56,12 +56,20 @@ class Case:
         return len(self.reqs)
 
 
-def build_case(s: synth.Spec, inputs: dict, layers, reqs, k_stride: Optional[int] = None,
+def build_case(s: synth.Spec, inputs, layers, reqs, k_stride: Optional[int] = None,
                host_kind: int = kv.KVOFF_HOST_COHERENT, two_regions: bool = True,
                with_pool_hits: bool = False, n_layers_ctx: Optional[int] = None,
-               stream=None) -> Case:
-    """Create a context, register the batch, upload and offload every (layer, request)."""
+               stream=None, keep=None) -> Case:
+    """Create a context, register the batch, upload and offload every (layer, request).
+
+    `inputs` is a dict (layer, r) -> synth.LayerRequest, or a function of
+    (layer, r) returning one; with a function, only the slices for which
+    keep(layer, r) is true are kept in Case.inputs after offloading."""
     layers = list(layers)
+    if callable(inputs):
+        get, inputs = inputs, {}
+    else:
+        get = inputs.__getitem__
     B = len(reqs)
     nb_max = max(rq.nb for rq in reqs)
     Kmax = max(min(rq.k, rq.nb) for rq in reqs)
@@ -74,14 +82,22 @@ def build_case(s: synth.Spec, inputs: dict, layers, reqs, k_stride: Optional[int
                           host_capacity_blocks=cap, host_mem_kind=host_kind)
     c = Case(s, layers, reqs, inputs, k_stride, ctx=ctx, nb_max=nb_max)
     c.rids = [kv.kvoff_register_request(ctx, rq.ctx) for rq in reqs]
+    pools = {}
     for l in layers:
         c.digest[l] = torch.empty((B, nb_max, s.Hkv, s.d), dtype=torch.float32, device="cuda")
-        c.q[l] = to_dev(np.stack([inputs[(l, r)].q for r in range(B)]))
+        qs = []
         for r in range(B):
-            lr = inputs[(l, r)]
+            lr = get((l, r))
+            qs.append(lr.q)
+            pools[(l, r)] = lr.pool
             kd, vd = to_dev(lr.K), to_dev(lr.V)
             kv.kvoff_offload_blocks(ctx, l, c.rids[r], kd, vd, c.digest[l][r], stream=stream)
+            torch.cuda.synchronize()
             del kd, vd
+            if keep is None or keep(l, r):
+                inputs[(l, r)] = lr
+        c.q[l] = to_dev(np.stack(qs))
+    c.inputs = inputs
     torch.cuda.synchronize()
     # slot pool: recall region(s) first, then the resident blocks of pool hits
     regions = 2 if two_regions else 1
@@ -92,7 +108,7 @@ def build_case(s: synth.Spec, inputs: dict, layers, reqs, k_stride: Optional[int
     if with_pool_hits:
         for l in layers:
             for r in range(B):
-                n_res += int(inputs[(l, r)].pool.sum())
+                n_res += int(pools[(l, r)].sum())
     c.n_slots = regions * n_recall + n_res
     rec = kv.kvoff_record_bytes(ctx)
     c.pool = torch.zeros(c.n_slots * rec, dtype=torch.uint8, device="cuda")
@@ -102,8 +118,7 @@ def build_case(s: synth.Spec, inputs: dict, layers, reqs, k_stride: Optional[int
             hit = np.zeros((B, nb_max), np.uint8)
             slot = np.full((B, nb_max), -1, np.int32)
             for r in range(B):
-                lr = inputs[(l, r)]
-                for b in np.flatnonzero(lr.pool):
+                for b in np.flatnonzero(pools[(l, r)]):
                     hit[r, b] = 1
                     slot[r, b] = nxt
                     # the resident copy is the same record bytes as the store's

@@ -33,6 +33,11 @@ def check_digests(c, l, slices):
             f"digest mismatch layer {l} req {r}: {np.argwhere(got != sl.D)[:5]}"
 
 
+def shared_set(sl, mode):
+    """The one block set of a shared-set mode (SoloHead or consensus)."""
+    return sl.sel_c if mode == kv.KVOFF_CONSENSUS else sl.sel
+
+
 def check_selection(c, l, mode, bufs, slices):
     sel = bufs.sel_idx.cpu().numpy()
     cnt = bufs.sel_cnt.cpu().numpy()
@@ -41,9 +46,10 @@ def check_selection(c, l, mode, bufs, slices):
         sl = slices[(l, r)]
         K, nb = sl.K, sl.lr.rq.nb
         assert cnt[r] == K, (l, r, cnt[r], K)
-        if mode == kv.KVOFF_SOLOHEAD:
-            assert np.allclose(sc[r, 0, :nb], sl.S, rtol=0, atol=1e-9 * (1 + np.abs(sl.S).max()))
-            assert sel[r, 0, :K].tolist() == sl.sel.tolist(), (l, r)
+        if mode in (kv.KVOFF_SOLOHEAD, kv.KVOFF_CONSENSUS):
+            S = sl.Sc if mode == kv.KVOFF_CONSENSUS else sl.S
+            assert np.allclose(sc[r, 0, :nb], S, rtol=0, atol=1e-9 * (1 + np.abs(S).max()))
+            assert sel[r, 0, :K].tolist() == shared_set(sl, mode).tolist(), (l, r)
             assert np.all(sel[r, 0, K:] == -1)
         else:
             for g in range(c.s.Hkv):
@@ -58,52 +64,69 @@ def expected_transfers(c, l, mode, slices, with_pool_hits):
     for r in range(c.B):
         sl = slices[(l, r)]
         hit = sl.lr.pool if with_pool_hits else None
-        sets = [sl.sel] if mode == kv.KVOFF_SOLOHEAD else list(sl.sel_g)
+        sets = list(sl.sel_g) if mode == kv.KVOFF_HEADWISE else [shared_set(sl, mode)]
         for s in sets:
             n_sel += len(s)
             miss = [b for b in s.tolist() if not (hit is not None and hit[b])]
             n_items += len(miss)
             n_hits += len(s) - len(miss)
-            if mode == kv.KVOFF_SOLOHEAD:
+            if mode != kv.KVOFF_HEADWISE:
                 n_tr += len(oracle.runs(s, hit)[0])
             else:
                 n_tr += oracle.headwise_transfers(s[None, :], [len(s)], hit)
     return dict(selected=n_sel, pool_hits=n_hits, items_recalled=n_items, transfers=n_tr)
 
 
-def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats=None):
+STAGE_CHUNK = 4 << 20  # bulk copy size of the staged engine
+
+
+def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats=None,
+                 engine=kv.KVOFF_ENGINE_ZEROCOPY):
+    """Recalled bytes and table entries.  Placement: the zero-copy and DMA
+    engines put rank i of request r at slot base + r*k_stride + i; the staged
+    engine puts the n-th recalled item of the call at slot base + n (slice
+    base*Hkv + n when headwise).  Resident blocks point at their pool slot."""
     s = c.s
+    compact = engine == kv.KVOFF_ENGINE_STAGED
     rec = kv.kvoff_record_bytes(c.ctx)
     slice_b = rec // s.Hkv
     pool = c.pool.cpu().numpy()
     table = bufs.table.cpu().numpy()
     base = c.recall_base[region]
     ps = c.pool_slot[l].cpu().numpy() if with_pool_hits else None
+    n_item = 0
     for r in range(c.B):
         sl = slices[(l, r)]
         K = sl.K
         hit = sl.lr.pool if with_pool_hits else np.zeros(sl.lr.rq.nb, np.uint8)
-        sets = [sl.sel] if mode == kv.KVOFF_SOLOHEAD else list(sl.sel_g)
+        sets = list(sl.sel_g) if mode == kv.KVOFF_HEADWISE else [shared_set(sl, mode)]
         for g, sset in enumerate(sets):
             want = workloads.block_records(sl, sset.tolist())  # [K][Hkv][2][bs][d]
             for i, b in enumerate(sset.tolist()):
                 ent = int(table[r, g, i])
-                if mode == kv.KVOFF_SOLOHEAD:
-                    exp_slot = int(ps[r, b]) if hit[b] else base + r * c.k_stride + i
-                    assert ent == exp_slot, (l, r, i, ent, exp_slot)
+                hw = mode == kv.KVOFF_HEADWISE
+                if hit[b]:
+                    exp = int(ps[r, b]) * (s.Hkv if hw else 1) + (g if hw else 0)
+                elif compact:
+                    exp = base * (s.Hkv if hw else 1) + n_item
+                    n_item += 1
+                else:
+                    exp = (base + r * c.k_stride + i) * (s.Hkv if hw else 1) + (g if hw else 0)
+                assert ent == exp, (l, r, g, i, ent, exp)
+                if not hw:
                     got = pool[ent * rec:(ent + 1) * rec]
                     assert np.array_equal(got, want[i].reshape(-1).view(np.uint8)), (l, r, i, b)
                 else:
-                    slot = int(ps[r, b]) if hit[b] else base + r * c.k_stride + i
-                    assert ent == slot * s.Hkv + g, (l, r, g, i, ent)
                     got = pool[ent * slice_b:(ent + 1) * slice_b]
                     assert np.array_equal(got, want[i, g].reshape(-1).view(np.uint8)), (l, r, g, i)
             assert np.all(table[r, g, K:] == -1)
     if stats is not None:
         exp = expected_transfers(c, l, mode, slices, with_pool_hits)
+        item = slice_b if mode == kv.KVOFF_HEADWISE else rec
+        if compact:  # bulk copies of the staging buffer
+            exp["transfers"] = -(-exp["items_recalled"] * item // STAGE_CHUNK)
         for k, v in exp.items():
             assert stats[k] == v, (k, stats[k], v)
-        item = rec if mode == kv.KVOFF_SOLOHEAD else slice_b
         assert stats["bytes"] == exp["items_recalled"] * item
 
 
@@ -113,10 +136,10 @@ def oracle_attention(c, l, mode, slices):
     for r in range(c.B):
         sl = slices[(l, r)]
         lr = sl.lr
-        if mode == kv.KVOFF_SOLOHEAD:
-            out[r] = oracle.attend_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, sl.sel)
-        else:
+        if mode == kv.KVOFF_HEADWISE:
             out[r] = oracle.attend_headwise_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, sl.sel_g)
+        else:
+            out[r] = oracle.attend_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, shared_set(sl, mode))
     return out
 
 

@@ -16,17 +16,17 @@ from tests import workloads
 pytestmark = pytest.mark.gpu
 
 
-def _slices(s, layers, reqs=None):
+def _slices(s, layers, reqs=None, lam=None):
     reqs = reqs or synth.request_draws(s)
     out = {}
     for l in layers:
         for r, rq in enumerate(reqs):
-            out[(l, r)] = workloads.make_slice(s, l, r, rq)
+            out[(l, r)] = workloads.make_slice(s, l, r, rq, lam=lam)
     return reqs, out
 
 
-def _case(s, layers, with_pool_hits=False, host_kind=kv.KVOFF_HOST_COHERENT, reqs=None):
-    reqs, sl = _slices(s, layers, reqs)
+def _case(s, layers, with_pool_hits=False, host_kind=kv.KVOFF_HOST_COHERENT, reqs=None, lam=None):
+    reqs, sl = _slices(s, layers, reqs, lam)
     inputs = {k: v.lr for k, v in sl.items()}
     c = H.build_case(s, inputs, layers, reqs, host_kind=host_kind, with_pool_hits=with_pool_hits)
     return c, sl
@@ -40,7 +40,7 @@ def _full_check(c, sl, l, mode, engine, with_pool_hits=False):
     torch.cuda.synchronize()
     P.check_digests(c, l, sl)
     P.check_selection(c, l, mode, bufs, sl)
-    P.check_recall(c, l, mode, bufs, sl, with_pool_hits=with_pool_hits, stats=stats)
+    P.check_recall(c, l, mode, bufs, sl, with_pool_hits=with_pool_hits, stats=stats, engine=engine)
     err = P.check_attention(c, l, mode, bufs, sl)
     return stats, err
 
@@ -48,7 +48,7 @@ def _full_check(c, sl, l, mode, engine, with_pool_hits=False):
 TINY = synth.spec(1)  # 1 request, 8/2 heads, 4096 tokens, bs 16, k 32, fp16
 
 
-@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
 def test_tiny_config_full_parity(engine):
     H.log(f"[tiny] engine {engine}")
     c, sl = _case(TINY, [0])
@@ -89,7 +89,7 @@ def test_offloaded_records_in_pinned_store():
 RAGGED = synth.spec(4, B=6, ctx_range=(700, 5000))
 
 
-@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
 def test_ragged_variable_parity(engine):
     H.log(f"[ragged] engine {engine}")
     c, sl = _case(RAGGED, [0])
@@ -107,7 +107,7 @@ HW = synth.spec(5, B=3, ctx=4096, k=16, hot=6)
 
 
 @pytest.mark.parametrize("mode", [kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE])
-@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
 def test_headwise_and_pool_hits(mode, engine):
     H.log(f"[headwise] mode {mode} engine {engine}")
     c, sl = _case(HW, [0], with_pool_hits=True)
@@ -119,15 +119,34 @@ def test_headwise_and_pool_hits(mode, engine):
         H.destroy(c)
 
 
+@pytest.mark.parametrize("lam", [0.5, 1.0])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
+def test_consensus_rule(lam, engine):
+    """The guide's max + lambda * mean consensus across KV heads as the shared set."""
+    H.log(f"[consensus] lambda {lam} engine {engine}")
+    c, sl = _case(HW, [0], with_pool_hits=True, lam=lam)
+    try:
+        kv.kvoff_set_consensus_lambda(c.ctx, lam)
+        stats, _ = _full_check(c, sl, 0, kv.KVOFF_CONSENSUS, engine, with_pool_hits=True)
+        H.log(f"  stats {stats}")
+        diff = sum(len(set(sl[(0, r)].sel_c.tolist()) ^ set(sl[(0, r)].sel.tolist()))
+                   for r in range(c.B))
+        H.log(f"  blocks differing from the summed-score set: {diff}")
+    finally:
+        H.destroy(c)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 2), (16, 16), (64, 4)])
 def test_group_sizes(Hq, Hkv):
     H.log(f"[groups] Hq {Hq} Hkv {Hkv}")
     s = synth.spec(2, B=2, Hq=Hq, Hkv=Hkv, ctx=2000, k=12, hot=5, headwise=Hkv > 1)
-    c, sl = _case(s, [0])
+    c, sl = _case(s, [0], lam=0.5)  # the context's default lambda
     try:
         _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
         if Hkv > 1:
             _full_check(c, sl, 0, kv.KVOFF_HEADWISE, kv.KVOFF_ENGINE_ZEROCOPY)
+        # consensus across KV heads (also for a single KV head: (1 + lambda) * S)
+        _full_check(c, sl, 0, kv.KVOFF_CONSENSUS, kv.KVOFF_ENGINE_ZEROCOPY)
     finally:
         H.destroy(c)
 
@@ -142,6 +161,8 @@ def test_degenerate_sizes():
     try:
         _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
         _full_check(c, sl, 0, kv.KVOFF_HEADWISE, kv.KVOFF_ENGINE_DMA)
+        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_STAGED)
+        _full_check(c, sl, 0, kv.KVOFF_HEADWISE, kv.KVOFF_ENGINE_STAGED)
     finally:
         H.destroy(c)
 
@@ -150,7 +171,7 @@ def test_degenerate_sizes():
 MULTI = synth.spec(3, B=2, L=4, ctx=3000, k=20, hot=8)
 
 
-@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
 def test_step_overlap_matches_serial_and_oracle(engine):
     H.log(f"[step] engine {engine}")
     layers = list(range(MULTI.L))
@@ -185,7 +206,12 @@ def test_step_overlap_matches_serial_and_oracle(engine):
             assert np.array_equal(serial.view(np.uint32), overlapped[l].view(np.uint32)), l
             P.check_attention_close(serial, P.oracle_attention(c, l, mode, sl), f"layer {l}")
         exp = [P.expected_transfers(c, l, mode, sl, False) for l in layers]
-        assert stats["transfers"] == sum(e["transfers"] for e in exp)
+        rec = kv.kvoff_record_bytes(c.ctx)
+        if engine == kv.KVOFF_ENGINE_STAGED:  # transfers are the bulk staging copies
+            want_tr = sum(-(-e["items_recalled"] * rec // P.STAGE_CHUNK) for e in exp)
+        else:
+            want_tr = sum(e["transfers"] for e in exp)
+        assert stats["transfers"] == want_tr
         assert stats["items_recalled"] == sum(e["items_recalled"] for e in exp)
     finally:
         H.destroy(c)

@@ -407,3 +407,28 @@ def test_gap_enforcement_redraws_a_tight_boundary():
     sl = workloads.condition(s, lr2, min_gap=want)
     assert sl.redraws >= 1 and sl.gap >= want
     assert lr2.attempts.sum() == sl.redraws
+
+
+# ----------------------------------------------------------- consensus rule
+
+def test_consensus_bruteforce_and_special_cases():
+    rng = np.random.default_rng(31)
+    Hq, Hkv, d, nb = 8, 4, 8, 6
+    q = _rand_bits(rng, (Hq, d), BF16)
+    D = rng.standard_normal((nb, Hkv, d)).astype(np.float32)
+    qv = _vals(q, BF16)
+    G = Hq // Hkv
+    for lam in (0.0, 0.5, 1.0):
+        S = oracle.score_consensus(q, BF16, D, lam)
+        for b in range(nb):
+            per = [sum(Fraction(float(qv[h, j])) * Fraction(float(D[b, g, j]))
+                       for h in range(g * G, (g + 1) * G) for j in range(d)) for g in range(Hkv)]
+            exact = max(per) + Fraction(lam) * sum(per) / Hkv
+            assert abs(Fraction(S[b]) - exact) <= Fraction(1e-12) * (1 + abs(exact))
+    # lambda = 0 is the per-block max over KV heads; one KV head gives (1 + lambda) * S
+    Sg = oracle.score_headwise(q, BF16, D)
+    assert np.array_equal(oracle.score_consensus(q, BF16, D, 0.0), Sg.max(axis=0))
+    q1 = _rand_bits(rng, (4, d), BF16)
+    D1 = rng.standard_normal((nb, 1, d)).astype(np.float32)
+    assert np.allclose(oracle.score_consensus(q1, BF16, D1, 0.5), 1.5 * oracle.score(q1, BF16, D1),
+                       rtol=1e-14, atol=0)

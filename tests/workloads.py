@@ -34,6 +34,9 @@ class Slice:
     sel_g: Optional[np.ndarray]   # [Hkv][K] ascending per-KV-head selections
     gap: float                    # smallest boundary gap over compared rankings
     redraws: int
+    Sc: Optional[np.ndarray] = None    # [nb] consensus scores (when lam is given)
+    sel_c: Optional[np.ndarray] = None  # [K] consensus selection
+    lam: Optional[float] = None
 
     @property
     def K(self) -> int:
@@ -50,7 +53,9 @@ def boundary(S: np.ndarray, K: int):
 
 
 def condition(s: synth.Spec, lr: synth.LayerRequest, min_gap: float = MIN_GAP,
-              headwise: Optional[bool] = None, enforce: bool = True) -> Slice:
+              headwise: Optional[bool] = None, enforce: bool = True,
+              lam: Optional[float] = None) -> Slice:
+    """lam: also condition and select the consensus ranking with that lambda."""
     headwise = s.headwise if headwise is None else headwise
     rq = lr.rq
     K = min(rq.k, rq.nb)
@@ -59,7 +64,9 @@ def condition(s: synth.Spec, lr: synth.LayerRequest, min_gap: float = MIN_GAP,
     while True:
         S = oracle.score(lr.q, s.dtype, D)
         Sg = oracle.score_headwise(lr.q, s.dtype, D) if headwise else None
-        rankings = [S] + ([Sg[g] for g in range(s.Hkv)] if headwise else [])
+        Sc = oracle.score_consensus(lr.q, s.dtype, D, lam) if lam is not None else None
+        rankings = [S] + ([Sg[g] for g in range(s.Hkv)] if headwise else []) + \
+            ([Sc] if Sc is not None else [])
         worst, bad = float("inf"), None
         for R in rankings:
             gap, b = boundary(R, K)
@@ -79,15 +86,16 @@ def condition(s: synth.Spec, lr: synth.LayerRequest, min_gap: float = MIN_GAP,
         D[bad] = oracle.digest(lr.K[t0:t1], s.dtype, s.bs)[0]
     sel = oracle.select(S, rq.k)
     sel_g = np.stack([oracle.select(Sg[g], rq.k) for g in range(s.Hkv)]) if headwise else None
-    return Slice(s, lr, D, S, Sg, sel, sel_g, worst, redraws)
+    sel_c = oracle.select(Sc, rq.k) if Sc is not None else None
+    return Slice(s, lr, D, S, Sg, sel, sel_g, worst, redraws, Sc, sel_c, lam)
 
 
 def make_slice(s: synth.Spec, layer: int, req: int, rq: Optional[synth.Request] = None,
-               enforce: bool = True) -> Slice:
+               enforce: bool = True, lam: Optional[float] = None) -> Slice:
     if rq is None:
         rq = synth.request_draws(s)[req]
     lr = synth.gen_layer_request(s, layer, req, rq)
-    return condition(s, lr, enforce=enforce)
+    return condition(s, lr, enforce=enforce, lam=lam)
 
 
 def block_records(sl: Slice, blocks) -> np.ndarray:
