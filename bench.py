@@ -39,9 +39,9 @@ METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM 
 # workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
 # and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
 # the recall source it was taken with: reported as null once that changes.
-GATHER_PMC = {"workload": (2, 4), "fetch_kib": 65662.45, "write_kib": 131076.02,
-              "fetch_scale": 1.9999, "write_scale": 1.0,
-              "recall_src_sha256": "65c7a1f5a4e71b8e1ea8466ec3fb511af7ba534385b9889ad58a1689bebe0a30"}
+GATHER_PMC = {"workload": (2, 4), "fetch_kib": 65662.40, "write_kib": 131076.02,
+              "fetch_scale": 1.9999, "write_scale": 1.0000,
+              "recall_src_sha256": "755b325f33a61e503127bc41acbc936143dcebe74ff8d43e1b0207a31c08a6cb"}
 
 
 def gather_traffic_bytes(config, layers):
@@ -75,7 +75,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-overlap", action="store_true",
                    help="skip the overlapped kvoff_step measurement (for clean kernel traces)")
-    p.add_argument("--report", choices=["fragmentation"], default=None,
+    p.add_argument("--report", choices=["fragmentation", "admission"], default=None,
                    help="instead of the bench line: recall of the headwise-vs-SoloHead "
                         "workload (per-KV-head vs shared block sets, 25%% pool hits) with "
                         "both engines: transfers, mean transfer size, GB/s")
@@ -219,6 +219,76 @@ def fragmentation_report(args):
     print(json.dumps(out), flush=True)
 
 
+def admission_report(args):
+    """IO-adaptive admission on the batch-8 decode step shape: measure the
+    link utilisation of an overlapped multi-layer step, let the policy pick
+    the layers to keep in HBM, pin them, and measure again."""
+    L = args.layers if args.layers != 4 else 8
+    sp = synth.spec(3, L=L)
+    reqs = synth.request_draws(sp)
+    B = len(reqs)
+    layers = list(range(L))
+    nb_tot = sum(rq.nb for rq in reqs)
+    case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                        layers, reqs, keep=lambda l, r: False, extra_slots=nb_tot * L)
+    mode, engine = kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY
+    sets = [H.make_buffers(case, mode) for _ in range(2)]
+    outs = [torch.empty_like(sets[0].out) for _ in layers]
+    hit = [torch.zeros((B, case.nb_max), dtype=torch.uint8, device="cuda") for _ in layers]
+    slot = [torch.full((B, case.nb_max), -1, dtype=torch.int32, device="cuda") for _ in layers]
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    topk = [rq.k for rq in reqs]
+
+    def step(want_stats=False):
+        return kv.kvoff_step(
+            case.ctx, layer_begin=0, layer_end=L, req_ids=case.rids, topk=topk, mode=mode,
+            engine=engine, k_stride=case.k_stride, q=[case.q[l] for l in layers],
+            digest=[case.digest[l] for l in layers], digest_stride=case.nb_max,
+            slot_pool=case.pool, n_slots=case.n_slots, recall_base_slot=case.recall_base,
+            scores=[b.scores for b in sets], sel_idx=[b.sel_idx for b in sets],
+            sel_cnt=[b.sel_cnt for b in sets], block_table=[b.table for b in sets],
+            scale=1.0 / math.sqrt(sp.d), out=outs, ws=sets[0].ws, pool_hit=hit,
+            pool_slot=slot, pool_stride=case.nb_max, compute_stream=compute, copy_stream=copy,
+            want_stats=want_stats)
+
+    def timed(n=6):
+        step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / n
+
+    st = step(want_stats=True)
+    sec = timed()
+    copy_peak, _ = link_peaks(case)
+    util = st["bytes"] / sec / (copy_peak * 1e9)
+    policy = kv.kvoff_admission_defaults()
+    resident = np.zeros(L, np.uint8)
+    n_res = kv.kvoff_admission_plan(policy, util, resident)
+    first = case.extra_base
+    rec_bytes = kv.kvoff_record_bytes(case.ctx)
+    for l in np.flatnonzero(resident).tolist():
+        for r, rq in enumerate(reqs):
+            kv.kvoff_make_resident(case.ctx, l, case.rids[r], case.pool, case.n_slots, first,
+                                   hit[l][r], slot[l][r])
+            first += rq.nb
+    torch.cuda.synchronize()
+    st2 = step(want_stats=True)
+    sec2 = timed()
+    out = {"workload": f"{sp.name}: batch {B}, {L} layers, context {reqs[0].ctx}, top-{reqs[0].k}",
+           "link_utilization": round(util, 4), "policy": {"low": policy.low, "high": policy.high,
+                                                          "max_offload": policy.max_offload},
+           "resident_layers": np.flatnonzero(resident).tolist(),
+           "hbm_bytes_resident": int(n_res * nb_tot * rec_bytes),
+           "before": {"layer_steps_per_s": round(L / sec, 2), "recalled_bytes": st["bytes"]},
+           "after": {"layer_steps_per_s": round(L / sec2, 2), "recalled_bytes": st2["bytes"],
+                     "pool_hits": st2["pool_hits"]}}
+    H.destroy(case)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -230,6 +300,8 @@ def main():
     torch.cuda.set_device(0)
     if args.report == "fragmentation":
         return fragmentation_report(args)
+    if args.report == "admission":
+        return admission_report(args)
     sp = synth.spec(args.config, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)

@@ -287,9 +287,60 @@ typedef struct kvoff_step_args {
   void* compute_stream;
   void* copy_stream;
   kvoff_stats* stats;                /* nullable: summed over layers; syncs    */
+  /* 0: recall and attend each layer's whole batch at once.  n > 0: per-request
+     interruptible scheduling (the guide's section "Interruptible Layer-Wise
+     Scheduling"): the batch is cut into contiguous groups of n requests,
+     each group's recall is followed on the compute stream by that group's
+     attention as soon as its own recall has landed, so attention of early
+     groups runs while later groups are still crossing the link.  Groups go
+     in ascending order of their selected-block count (fewest first).
+     Outputs are identical to n = 0. */
+  int32_t group_requests;
 } kvoff_step_args;
 
 int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* args);
+
+/* ------------------------------------------------------------- admission */
+
+/* IO-adaptive offloading admission ("PulseInfer Guide", aiFetchly, section
+ * "Interruptible Layer-Wise Scheduling & Adaptive Admission"; abstract:
+ * IO-Adaptive Offloading Admission adapts offloading decisions): with the
+ * host link lightly used the store takes up to max_offload of the layers;
+ * near saturation the most active layers (the first and the last) are kept
+ * in HBM.  Resident layers are recalled from HBM: their blocks are pool hits. */
+typedef struct kvoff_admission_policy {
+  double low;          /* utilisation below which layers are released (0.50)   */
+  double high;         /* utilisation above which more layers are pinned (0.85) */
+  double max_offload;  /* largest offloaded fraction of the layers (0.90)      */
+  int32_t step_layers; /* layers pinned or released per decision (2)           */
+} kvoff_admission_policy;
+
+/* Fills *p with the defaults above. */
+void kvoff_admission_defaults(kvoff_admission_policy* p);
+
+/* One admission decision.  utilization = recalled bytes / (elapsed seconds *
+ * link peak) over the last window.  resident [num_layers] is the current plan
+ * on entry (1 = kept in HBM) and the new plan on return.  Layers are pinned
+ * in the order 0, L-1, 1, L-2, ... and released in the reverse order; at
+ * least ceil((1 - max_offload) * num_layers) stay resident.  *n_resident
+ * receives the new count.  Pure host logic.  Errors: EINVAL. */
+int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, double utilization,
+                         uint8_t* resident, int32_t* n_resident);
+
+/* Makes (layer, req_id) resident: one bulk hipMemcpyAsync of its nb records
+ * from the pinned store into HBM slots [first_slot, first_slot + nb) of
+ * slot_pool_dev, then sets pool_hit_dev[b] = 1 and pool_slot_dev[b] =
+ * first_slot + b for b < nb (the request's row of the maps kvoff_recall
+ * takes).  Errors: EINVAL, ERANGE (slots past n_slots), ESTATE (layer not
+ * offloaded), EHIP. */
+int kvoff_make_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, void* slot_pool_dev,
+                        int64_t n_slots, int64_t first_slot, uint8_t* pool_hit_dev,
+                        int32_t* pool_slot_dev, void* stream);
+
+/* Releases (layer, req_id): clears pool_hit_dev[b] for b < nb, so the next
+ * recall moves its blocks from the store again.  Errors: EINVAL, ESTATE. */
+int kvoff_release_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, uint8_t* pool_hit_dev,
+                           void* stream);
 
 /* ------------------------------------------------------------- diagnostics */
 

@@ -34,7 +34,8 @@ EXPORTS = (
     "kvoff_register_request",
     "kvoff_host_record", "kvoff_offload_blocks", "kvoff_select", "kvoff_recall",
     "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_read",
-    "kvoff_strerror", "kvoff_last_error",
+    "kvoff_strerror", "kvoff_last_error", "kvoff_admission_defaults", "kvoff_admission_plan",
+    "kvoff_make_resident", "kvoff_release_resident",
 )
 
 
@@ -52,6 +53,11 @@ class kvoff_config(ctypes.Structure):
         ("max_requests", ctypes.c_int32), ("host_mem_kind", ctypes.c_int32),
         ("host_capacity_blocks", ctypes.c_int64),
     ]
+
+
+class kvoff_admission_policy(ctypes.Structure):
+    _fields_ = [("low", ctypes.c_double), ("high", ctypes.c_double),
+                ("max_offload", ctypes.c_double), ("step_layers", ctypes.c_int32)]
 
 
 class kvoff_stats(ctypes.Structure):
@@ -80,6 +86,7 @@ class kvoff_step_args(ctypes.Structure):
         ("scale", ctypes.c_float), ("out_dev", _vp),
         ("ws_dev", _vp), ("ws_bytes", ctypes.c_size_t),
         ("compute_stream", _vp), ("copy_stream", _vp), ("stats", _vp),
+        ("group_requests", ctypes.c_int32),
     ]
 
 
@@ -113,6 +120,11 @@ def lib() -> ctypes.CDLL:
     L.kvoff_workspace_size.restype = sz
     L.kvoff_step.argtypes = [_vp, P(kvoff_step_args)]
     L.kvoff_probe_read.argtypes = [_vp, i64, _vp, i32, _vp]
+    L.kvoff_admission_defaults.argtypes = [P(kvoff_admission_policy)]
+    L.kvoff_admission_defaults.restype = None
+    L.kvoff_admission_plan.argtypes = [P(kvoff_admission_policy), i32, ctypes.c_double, _vp, P(i32)]
+    L.kvoff_make_resident.argtypes = [_vp, i32, i32, _vp, i64, i64, _vp, _vp, _vp]
+    L.kvoff_release_resident.argtypes = [_vp, i32, i32, _vp, _vp]
     L.kvoff_strerror.argtypes = [ctypes.c_int]
     L.kvoff_strerror.restype = ctypes.c_char_p
     L.kvoff_last_error.argtypes = []
@@ -120,7 +132,8 @@ def lib() -> ctypes.CDLL:
     for name in ("kvoff_create", "kvoff_destroy", "kvoff_register_request", "kvoff_host_record",
                  "kvoff_set_consensus_lambda",
                  "kvoff_offload_blocks", "kvoff_select", "kvoff_recall", "kvoff_sparse_decode",
-                 "kvoff_step", "kvoff_probe_read"):
+                 "kvoff_step", "kvoff_probe_read", "kvoff_admission_plan", "kvoff_make_resident",
+                 "kvoff_release_resident"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -243,7 +256,7 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
                sel_cnt: Sequence, block_table: Sequence, scale: float, out: Sequence, ws,
                pool_hit: Optional[Sequence] = None, pool_slot: Optional[Sequence] = None,
                pool_stride: int = 0, compute_stream=None, copy_stream=None,
-               want_stats: bool = False) -> Optional[dict]:
+               want_stats: bool = False, group_requests: int = 0) -> Optional[dict]:
     n_layers = layer_end - layer_begin
     ids, tk = _i32_array(req_ids), _i32_array(topk)
     arr = lambda ts: (_vp * max(n_layers, 1))(*[_ptr(t) for t in ts])
@@ -278,9 +291,34 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
     a.copy_stream = _stream(copy_stream) if copy_stream is not None else cs
     st = kvoff_stats() if want_stats else None
     a.stats = ctypes.cast(ctypes.pointer(st), _vp) if st is not None else None
+    a.group_requests = group_requests
     _check(lib().kvoff_step(ctx, ctypes.byref(a)))
     return st.as_dict() if st is not None else None
 
 
 def kvoff_probe_read(ptr, n_bytes: int, sink, n_wg: int = 0, stream=None) -> None:
     _check(lib().kvoff_probe_read(_ptr(ptr), n_bytes, _ptr(sink), n_wg, _stream(stream)))
+
+
+def kvoff_admission_defaults() -> kvoff_admission_policy:
+    p = kvoff_admission_policy()
+    lib().kvoff_admission_defaults(ctypes.byref(p))
+    return p
+
+
+def kvoff_admission_plan(policy: kvoff_admission_policy, utilization: float, resident) -> int:
+    """resident: numpy uint8 [num_layers], updated in place; returns the count."""
+    n = ctypes.c_int32()
+    _check(lib().kvoff_admission_plan(ctypes.byref(policy), len(resident), utilization,
+                                      resident.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n)))
+    return n.value
+
+
+def kvoff_make_resident(ctx: int, layer: int, req_id: int, slot_pool, n_slots: int,
+                        first_slot: int, pool_hit, pool_slot, stream=None) -> None:
+    _check(lib().kvoff_make_resident(ctx, layer, req_id, _ptr(slot_pool), n_slots, first_slot,
+                                     _ptr(pool_hit), _ptr(pool_slot), _stream(stream)))
+
+
+def kvoff_release_resident(ctx: int, layer: int, req_id: int, pool_hit, stream=None) -> None:
+    _check(lib().kvoff_release_resident(ctx, layer, req_id, _ptr(pool_hit), _stream(stream)))

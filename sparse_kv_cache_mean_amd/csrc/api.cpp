@@ -155,6 +155,7 @@ int kvoff_destroy(kvoff_ctx* ctx) {
     if (ctx->ev_rec[i]) (void)hipEventDestroy(ctx->ev_rec[i]);
   }
   stage_pool_destroy(ctx);
+  for (hipEvent_t e : ctx->ev_group) (void)hipEventDestroy(e);
   if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
   if (ctx->stage_buf) (void)hipHostFree(ctx->stage_buf);
   if (ctx->table_host) (void)hipHostFree(ctx->table_host);
@@ -194,6 +195,7 @@ int kvoff_register_request(kvoff_ctx* ctx, int64_t n_tokens, int32_t* req_id) {
   KVOFF_HIP(hipMemcpy(ctx->d_reqs + id, &d, sizeof d, hipMemcpyHostToDevice));
   ctx->reqs.push_back(h);
   ctx->offloaded.resize(ctx->reqs.size() * (size_t)ctx->cfg.num_layers, 0);
+  ctx->resident.resize(ctx->reqs.size() * (size_t)ctx->cfg.num_layers, 0);
   ctx->store_used += need;
   *req_id = id;
   return KVOFF_OK;

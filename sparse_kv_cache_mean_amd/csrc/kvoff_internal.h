@@ -51,6 +51,7 @@ struct kvoff_ctx {
   int64_t store_used = 0;   // records reserved so far
   std::vector<kvoff::ReqHost> reqs;
   std::vector<uint8_t> offloaded;  // [req][layer]: offload enqueued
+  std::vector<uint8_t> resident;   // [req][layer]: pinned in HBM by kvoff_make_resident
   kvoff::ReqDev* d_reqs = nullptr; // device copy of the request table
   unsigned long long* d_counters = nullptr;  // recall statistics (device)
   hipEvent_t ev_sel[2] = {nullptr, nullptr};
@@ -62,6 +63,7 @@ struct kvoff_ctx {
   void* table_host = nullptr;               // pinned block-table staging
   size_t table_cap = 0;
   hipEvent_t ev_stage = nullptr;            // behind the last staged copy
+  std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
   bool ev_stage_pending = false;
 };
 

@@ -105,6 +105,21 @@ __device__ __forceinline__ void write_table_and_count(const GatherArgs& a, int64
   }
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const u32x4_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(u32x4_t* p, u32x4_t v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// NTL / NTS: nontemporal hint on the host-link loads / the HBM stores
+template <bool NTL, bool NTS>
 __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(GatherArgs a) {
   const int tid = threadIdx.x;
   for (int64_t p = blockIdx.x; p < a.n_pieces; p += gridDim.x) {
@@ -118,17 +133,18 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(GatherArgs a) {
                          (a.hw ? (int64_t)it.g * a.item_bytes : 0) + (int64_t)piece * a.piece_bytes;
     uint8_t* dst = a.pool + (a.hw ? (it.slot * a.Hkv + it.g) * a.item_bytes : it.slot * a.rec_bytes) +
                    (int64_t)piece * a.piece_bytes;
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
+    u32x4_t* d4 = reinterpret_cast<u32x4_t*>(dst);
     const int n16 = (int)(a.piece_bytes / 16);  // 1024 or 512 (multiple of 256)
     if (n16 == 1024) {
-      uint4 x0 = s4[tid], x1 = s4[tid + 256], x2 = s4[tid + 512], x3 = s4[tid + 768];
-      d4[tid] = x0;
-      d4[tid + 256] = x1;
-      d4[tid + 512] = x2;
-      d4[tid + 768] = x3;
+      const u32x4_t x0 = ld16<NTL>(s4 + tid), x1 = ld16<NTL>(s4 + tid + 256),
+                    x2 = ld16<NTL>(s4 + tid + 512), x3 = ld16<NTL>(s4 + tid + 768);
+      st16<NTS>(d4 + tid, x0);
+      st16<NTS>(d4 + tid + 256, x1);
+      st16<NTS>(d4 + tid + 512, x2);
+      st16<NTS>(d4 + tid + 768, x3);
     } else {
-      for (int k = tid; k < n16; k += GATHER_THREADS) d4[k] = s4[k];
+      for (int k = tid; k < n16; k += GATHER_THREADS) st16<NTS>(d4 + k, ld16<NTL>(s4 + k));
     }
   }
 }
@@ -158,6 +174,18 @@ __global__ __launch_bounds__(256) void probe_kernel(const uint4* src, int64_t n1
     for (int k = 0; k < 4; ++k) acc ^= x[k].x ^ x[k].y ^ x[k].z ^ x[k].w;
   }
   sink[threadIdx.x] = acc;
+}
+
+// KVOFF_GATHER_NT: bit 0 = nontemporal host loads, bit 1 = nontemporal HBM
+// stores.  Default 0: neither changes the link rate (56.9 GB/s measured
+// either way) and nontemporal stores keep the records out of L2, which the
+// attention that follows would otherwise hit.
+int gather_nt() {
+  static int v = [] {
+    const char* e = std::getenv("KVOFF_GATHER_NT");
+    return e ? (std::atoi(e) & 3) : 0;
+  }();
+  return v;
 }
 
 int gather_grid_cap() {
@@ -212,7 +240,12 @@ int launch_gather(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, 
   if (a.n_pieces == 0) return KVOFF_OK;
   const int64_t cap = gather_grid_cap();
   const unsigned grid = (unsigned)(a.n_pieces < cap ? a.n_pieces : cap);
-  hipLaunchKernelGGL(gather_kernel, dim3(grid), dim3(GATHER_THREADS), 0, stream, a);
+  switch (gather_nt()) {
+    case 1: hipLaunchKernelGGL((gather_kernel<true, false>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((gather_kernel<false, true>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((gather_kernel<true, true>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
+    default: hipLaunchKernelGGL((gather_kernel<false, false>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
+  }
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }

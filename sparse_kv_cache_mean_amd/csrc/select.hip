@@ -28,15 +28,20 @@
 namespace kvoff {
 namespace {
 
-// blocks per wave of score_kernel (digest rows in flight per lane: BPW * NC)
-int score_bpw() {
-  static const int v = [] {
-    const char* e = std::getenv("KVOFF_SCORE_BPW");
-    const int x = e ? std::atoi(e) : 0;
-    return x == 2 || x == 4 || x == 8 ? x : 4;
+// blocks per wave of score_kernel (measured: 2 and 4 equal, 8 slower)
+constexpr int SCORE_BPW = 2;
+constexpr int SCORE_WG_BLOCKS = 4 * SCORE_BPW;
+
+// digest loads with the nontemporal hint (KVOFF_SCORE_NT=0 turns it off)
+bool score_nt() {
+  static const bool v = [] {
+    const char* e = std::getenv("KVOFF_SCORE_NT");
+    return !(e && e[0] == '0');
   }();
   return v;
 }
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct ScoreArgs {
   BatchIds batch;
@@ -57,9 +62,8 @@ __device__ __forceinline__ double widen_t(uint16_t h) {
   else return (double)__builtin_bit_cast(_Float16, h);
 }
 
-template <int NC, int MODE, bool BF16, int SCORE_BPW>
+template <int NC, int MODE, bool BF16, bool NT>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  constexpr int SCORE_WG_BLOCKS = 4 * SCORE_BPW;
   __shared__ double u_s[NC * 256];
   extern __shared__ uint4 q_s[];  // the request's q rows, Hq * 16 chunks of 16 bytes
   const int r = blockIdx.y;
@@ -86,7 +90,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int idx = min(c * 256 + lane * 4, F - 4);
-      v[k][c] = *reinterpret_cast<const float4*>(dr + b * F + idx);
+      const f32x4_t* p = reinterpret_cast<const f32x4_t*>(dr + b * F + idx);
+      f32x4_t x;
+      if constexpr (NT)
+        x = __builtin_nontemporal_load(p);
+      else
+        x = *p;
+      v[k][c] = make_float4(x[0], x[1], x[2], x[3]);
     }
   }
   // q rows: 4 chunks of 16 bytes per thread (Hq <= 64 in one round); the
@@ -338,23 +348,22 @@ void topk_launch(const TopkArgs& a, dim3 grid, bool hw, hipStream_t s) {
     hipLaunchKernelGGL((topk_kernel<false, KPT>), grid, dim3(256), 0, s, a);
 }
 
-template <int NC, int MODE, int BPW>
+template <int NC, int MODE, bool NT>
 void score_launch_b(const ScoreArgs& a, int64_t max_nb, hipStream_t s) {
   const size_t lds = std::max<size_t>((size_t)a.Hq * kHeadDim * 2, 4 * 256 * 16);  // staged q rows
-  const dim3 grid((unsigned)((max_nb + 4 * BPW - 1) / (4 * BPW)), (unsigned)a.batch.n);
+  const dim3 grid((unsigned)((max_nb + SCORE_WG_BLOCKS - 1) / SCORE_WG_BLOCKS), (unsigned)a.batch.n);
   if (a.bf16)
-    hipLaunchKernelGGL((score_kernel<NC, MODE, true, BPW>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((score_kernel<NC, MODE, true, NT>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((score_kernel<NC, MODE, false, BPW>), grid, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((score_kernel<NC, MODE, false, NT>), grid, dim3(256), lds, s, a);
 }
 
 template <int NC, int MODE>
 void score_launch_m(const ScoreArgs& a, int64_t max_nb, hipStream_t s) {
-  switch (score_bpw()) {
-    case 2: score_launch_b<NC, MODE, 2>(a, max_nb, s); break;
-    case 8: score_launch_b<NC, MODE, 8>(a, max_nb, s); break;
-    default: score_launch_b<NC, MODE, 4>(a, max_nb, s); break;
-  }
+  if (score_nt())
+    score_launch_b<NC, MODE, true>(a, max_nb, s);
+  else
+    score_launch_b<NC, MODE, false>(a, max_nb, s);
 }
 
 template <int NC>

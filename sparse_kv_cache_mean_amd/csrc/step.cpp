@@ -13,7 +13,17 @@
 // select(l+2) is enqueued on the compute stream after attend(l) and
 // recall(l+2) waits for select(l+2).  Every kernel reads exactly the data a
 // serial run would, so outputs are bit-identical to the serial order.
+//
+// With group_requests > 0 each layer's recall and attention are issued per
+// contiguous request group, every group's attention waiting only for its own
+// recall: the per-request form of the guide's interruptible layer-wise
+// scheduling.  Within a layer the groups go in ascending order of the blocks
+// they must transfer (selected blocks of requests not pinned in HBM for that
+// layer by kvoff_make_resident), so groups already in HBM are attended while
+// the others are still crossing the link.
+#include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "kvoff_internal.h"
 
@@ -27,8 +37,8 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
                 ctx->cfg.num_layers);
   if (A->stats) memset(A->stats, 0, sizeof *A->stats);
   if (L == 0 || A->n_req == 0) return KVOFF_OK;
-  if (!A->q_dev || !A->digest_dev || !A->out_dev)
-    return fail(KVOFF_EINVAL, "q_dev, digest_dev and out_dev arrays must be non-NULL");
+  if (!A->q_dev || !A->digest_dev || !A->out_dev || !A->req_ids || !A->topk)
+    return fail(KVOFF_EINVAL, "q_dev, digest_dev, out_dev, req_ids and topk must be non-NULL");
   for (int i = 0; i < 2; ++i)
     if (!A->scores_dev[i] || !A->sel_idx_dev[i] || !A->sel_cnt_dev[i] || !A->block_table_dev[i])
       return fail(KVOFF_EINVAL, "buffer set %d has a NULL buffer", i);
@@ -49,33 +59,85 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     KVOFF_HIP(hipEventRecord(ctx->ev_sel[buf], cs));
     return KVOFF_OK;
   };
+  // request groups (one group = the whole batch unless group_requests > 0)
+  struct Group {
+    int r0, n;
+  };
+  std::vector<Group> groups;
+  const int gsz = A->group_requests > 0 ? A->group_requests : A->n_req;
+  for (int r0 = 0; r0 < A->n_req; r0 += gsz) {
+    groups.push_back(Group{r0, std::min(gsz, A->n_req - r0)});
+    for (int r = r0; r < r0 + groups.back().n; ++r)
+      if (A->req_ids[r] < 0 || A->req_ids[r] >= (int)ctx->reqs.size())
+        return fail(KVOFF_ESTATE, "request id %d is not registered", A->req_ids[r]);
+  }
+  // issue order of the groups for layer li: fewest blocks to transfer first
+  // (stable, so equal groups keep batch order)
+  auto order_for = [&](int li) {
+    const int layer = A->layer_begin + li;
+    std::vector<int64_t> key(groups.size(), 0);
+    for (size_t gi = 0; gi < groups.size(); ++gi)
+      for (int r = groups[gi].r0; r < groups[gi].r0 + groups[gi].n; ++r) {
+        const int id = A->req_ids[r];
+        if (!ctx->resident[(size_t)id * ctx->cfg.num_layers + layer])
+          key[gi] += std::min<int64_t>(A->topk[r], ctx->reqs[id].nb);
+      }
+    std::vector<int> ord(groups.size());
+    for (size_t gi = 0; gi < groups.size(); ++gi) ord[gi] = (int)gi;
+    std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) { return key[a] < key[b]; });
+    return ord;
+  };
+  const size_t n_ev = 2 * groups.size();
+  while (ctx->ev_group.size() < n_ev) {
+    hipEvent_t e;
+    KVOFF_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    ctx->ev_group.push_back(e);
+  }
+  const int sets = A->mode == KVOFF_HEADWISE ? ctx->cfg.num_kv_heads : 1;
+  const int64_t q_row = (int64_t)ctx->cfg.num_q_heads * ctx->cfg.head_dim;  // elements per request
+
   auto recall_l = [&](int li) -> int {
     const int buf = li & 1;
     KVOFF_HIP(hipStreamWaitEvent(xs, ctx->ev_sel[buf], 0));
-    kvoff_stats st_l;
-    int st = kvoff_recall(ctx, A->layer_begin + li, A->n_req, A->req_ids, A->mode,
-                          A->sel_idx_dev[buf], A->sel_cnt_dev[buf], A->k_stride,
-                          A->pool_hit_dev ? A->pool_hit_dev[li] : nullptr,
-                          A->pool_slot_dev ? A->pool_slot_dev[li] : nullptr, A->pool_stride,
-                          A->slot_pool_dev, A->n_slots, A->recall_base_slot[buf],
-                          A->block_table_dev[buf], A->engine, A->stats ? &st_l : nullptr, xs);
-    if (st) return st;
-    if (A->stats) {
-      A->stats->selected += st_l.selected;
-      A->stats->pool_hits += st_l.pool_hits;
-      A->stats->items_recalled += st_l.items_recalled;
-      A->stats->transfers += st_l.transfers;
-      A->stats->bytes += st_l.bytes;
+    for (int gi : order_for(li)) {
+      const Group& g = groups[gi];
+      const int64_t sel_off = (int64_t)g.r0 * sets * A->k_stride;
+      kvoff_stats st_l;
+      int st = kvoff_recall(
+          ctx, A->layer_begin + li, g.n, A->req_ids + g.r0, A->mode, A->sel_idx_dev[buf] + sel_off,
+          A->sel_cnt_dev[buf] + g.r0, A->k_stride,
+          A->pool_hit_dev ? A->pool_hit_dev[li] + (int64_t)g.r0 * A->pool_stride : nullptr,
+          A->pool_slot_dev ? A->pool_slot_dev[li] + (int64_t)g.r0 * A->pool_stride : nullptr,
+          A->pool_stride, A->slot_pool_dev, A->n_slots,
+          A->recall_base_slot[buf] + (int64_t)g.r0 * A->k_stride, A->block_table_dev[buf] + sel_off,
+          A->engine, A->stats ? &st_l : nullptr, xs);
+      if (st) return st;
+      if (A->stats) {
+        A->stats->selected += st_l.selected;
+        A->stats->pool_hits += st_l.pool_hits;
+        A->stats->items_recalled += st_l.items_recalled;
+        A->stats->transfers += st_l.transfers;
+        A->stats->bytes += st_l.bytes;
+      }
+      KVOFF_HIP(hipEventRecord(ctx->ev_group[buf * groups.size() + gi], xs));
     }
-    KVOFF_HIP(hipEventRecord(ctx->ev_rec[buf], xs));
     return KVOFF_OK;
   };
   auto attend_l = [&](int li) -> int {
     const int buf = li & 1;
-    KVOFF_HIP(hipStreamWaitEvent(cs, ctx->ev_rec[buf], 0));
-    return kvoff_sparse_decode(ctx, A->n_req, A->req_ids, A->mode, A->q_dev[li], A->slot_pool_dev,
-                               A->block_table_dev[buf], A->sel_idx_dev[buf], A->sel_cnt_dev[buf],
-                               A->k_stride, A->scale, A->out_dev[li], A->ws_dev, A->ws_bytes, cs);
+    for (int gi : order_for(li)) {
+      const Group& g = groups[gi];
+      const int64_t sel_off = (int64_t)g.r0 * sets * A->k_stride;
+      KVOFF_HIP(hipStreamWaitEvent(cs, ctx->ev_group[buf * groups.size() + gi], 0));
+      int st = kvoff_sparse_decode(
+          ctx, g.n, A->req_ids + g.r0, A->mode,
+          (const uint8_t*)A->q_dev[li] + g.r0 * q_row * 2, A->slot_pool_dev,
+          A->block_table_dev[buf] + sel_off, A->sel_idx_dev[buf] + sel_off,
+          A->sel_cnt_dev[buf] + g.r0, A->k_stride, A->scale, A->out_dev[li] + g.r0 * q_row,
+          A->ws_dev, A->ws_bytes, cs);
+      if (st) return st;
+    }
+    return KVOFF_OK;
   };
 
   int st;

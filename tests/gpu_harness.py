@@ -48,6 +48,7 @@ class Case:
     n_slots: int = 0
     recall_base: tuple = (0, 0)
     resident_base: int = 0
+    extra_base: int = 0            # first slot after the recall regions and pool hits
     pool_hit: dict = field(default_factory=dict)   # layer -> [B][nb_max] uint8
     pool_slot: dict = field(default_factory=dict)  # layer -> [B][nb_max] int32
 
@@ -59,7 +60,7 @@ class Case:
 def build_case(s: synth.Spec, inputs, layers, reqs, k_stride: Optional[int] = None,
                host_kind: int = kv.KVOFF_HOST_COHERENT, two_regions: bool = True,
                with_pool_hits: bool = False, n_layers_ctx: Optional[int] = None,
-               stream=None, keep=None) -> Case:
+               stream=None, keep=None, extra_slots: int = 0) -> Case:
     """Create a context, register the batch, upload and offload every (layer, request).
 
     `inputs` is a dict (layer, r) -> synth.LayerRequest, or a function of
@@ -109,7 +110,8 @@ def build_case(s: synth.Spec, inputs, layers, reqs, k_stride: Optional[int] = No
         for l in layers:
             for r in range(B):
                 n_res += int(pools[(l, r)].sum())
-    c.n_slots = regions * n_recall + n_res
+    c.n_slots = regions * n_recall + n_res + extra_slots
+    c.extra_base = regions * n_recall + n_res
     rec = kv.kvoff_record_bytes(ctx)
     c.pool = torch.zeros(c.n_slots * rec, dtype=torch.uint8, device="cuda")
     if with_pool_hits:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared():
     with open(os.path.join(ROOT, "include", "kvoff.h")) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const char\*|int64_t|size_t|int)\s+(kvoff_\w+)\(",
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int64_t|size_t|int|void)\s+(kvoff_\w+)\(",
                                  text, re.M)))
 
 

@@ -217,6 +217,85 @@ def test_step_overlap_matches_serial_and_oracle(engine):
         H.destroy(c)
 
 
+RAGGED_LAYERS = synth.spec(4, B=6, L=2, ctx_range=(700, 5000))
+
+
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
+def test_step_request_groups_match_whole_batch(engine):
+    """Interruptible per-request-group scheduling gives the same bits as one
+    recall and one attention per layer, and both match the oracle."""
+    H.log(f"[step groups] engine {engine}")
+    s = RAGGED_LAYERS
+    layers = [0, 1]
+    c, sl = _case(s, layers)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        sets = [H.make_buffers(c, mode) for _ in range(2)]
+        compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+        results = {}
+        for grp in (0, 1, 4):
+            outs = [torch.full((c.B, s.Hq, s.d), float("nan"), device="cuda") for _ in layers]
+            st = kv.kvoff_step(
+                c.ctx, layer_begin=0, layer_end=2, req_ids=c.rids, topk=[rq.k for rq in c.reqs],
+                mode=mode, engine=engine, k_stride=c.k_stride, q=[c.q[l] for l in layers],
+                digest=[c.digest[l] for l in layers], digest_stride=c.nb_max, slot_pool=c.pool,
+                n_slots=c.n_slots, recall_base_slot=c.recall_base,
+                scores=[b.scores for b in sets], sel_idx=[b.sel_idx for b in sets],
+                sel_cnt=[b.sel_cnt for b in sets], block_table=[b.table for b in sets],
+                scale=1.0 / math.sqrt(s.d), out=outs, ws=sets[0].ws, compute_stream=compute,
+                copy_stream=copy, want_stats=True, group_requests=grp)
+            torch.cuda.synchronize()
+            results[grp] = ([o.cpu().numpy() for o in outs], st)
+        for grp in (1, 4):
+            for l in layers:
+                assert np.array_equal(results[grp][0][l].view(np.uint32),
+                                      results[0][0][l].view(np.uint32)), (grp, l)
+            assert results[grp][1]["items_recalled"] == results[0][1]["items_recalled"]
+        for l in layers:
+            P.check_attention_close(results[0][0][l], P.oracle_attention(c, l, mode, sl), f"layer {l}")
+    finally:
+        H.destroy(c)
+
+
+def test_resident_layer_is_not_recalled():
+    """IO-adaptive admission: a layer made resident in HBM recalls nothing and
+    attends to the same bytes; releasing it brings the recall back."""
+    H.log("[admission] resident layer")
+    s = synth.spec(2, B=3, ctx=3000, k=20, hot=8)
+    reqs, sl = _slices(s, [0])
+    nb_tot = sum(rq.nb for rq in reqs)
+    c = H.build_case(s, {k: v.lr for k, v in sl.items()}, [0], reqs, extra_slots=nb_tot)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        bufs = H.make_buffers(c, mode)
+        st0 = H.run_layer(c, 0, mode, bufs, want_stats=True)
+        torch.cuda.synchronize()
+        out0 = bufs.out.cpu().numpy().copy()
+        hit = torch.zeros((c.B, c.nb_max), dtype=torch.uint8, device="cuda")
+        slot = torch.full((c.B, c.nb_max), -1, dtype=torch.int32, device="cuda")
+        first = c.extra_base
+        for r, rq in enumerate(reqs):
+            kv.kvoff_make_resident(c.ctx, 0, c.rids[r], c.pool, c.n_slots, first, hit[r], slot[r])
+            first += rq.nb
+        c.pool_hit[0], c.pool_slot[0] = hit, slot
+        st1 = H.run_layer(c, 0, mode, bufs, with_pool_hits=True, want_stats=True)
+        torch.cuda.synchronize()
+        assert st1["items_recalled"] == 0 and st1["bytes"] == 0
+        assert st1["pool_hits"] == st0["selected"]
+        assert np.array_equal(bufs.out.cpu().numpy().view(np.uint32), out0.view(np.uint32))
+        for r in range(c.B):
+            kv.kvoff_release_resident(c.ctx, 0, c.rids[r], hit[r])
+        st2 = H.run_layer(c, 0, mode, bufs, with_pool_hits=True, want_stats=True)
+        torch.cuda.synchronize()
+        assert st2["items_recalled"] == st0["items_recalled"]
+        assert np.array_equal(bufs.out.cpu().numpy().view(np.uint32), out0.view(np.uint32))
+        with pytest.raises(kv.KvoffError) as e:  # slots past the pool
+            kv.kvoff_make_resident(c.ctx, 0, c.rids[0], c.pool, c.n_slots, c.n_slots - 1, hit[0], slot[0])
+        assert e.value.status == kv.KVOFF_ERANGE
+    finally:
+        H.destroy(c)
+
+
 def test_error_paths_on_device():
     H.log("[errors]")
     s = synth.spec(1, ctx=512, k=8, hot=2)
