@@ -71,6 +71,8 @@ def parse():
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--engine", choices=["zerocopy", "dma", "staged"], default="zerocopy")
     p.add_argument("--host-mem", choices=["coherent", "noncoherent"], default="coherent")
+    p.add_argument("--attn-qk", choices=["mfma", "valu"], default="mfma",
+                   help="what computes the attention's QK^T")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-overlap", action="store_true",
@@ -318,6 +320,7 @@ def main():
               "staged": kv.KVOFF_ENGINE_STAGED}[args.engine]
     host_kind = kv.KVOFF_HOST_NONCOHERENT if args.host_mem == "noncoherent" else kv.KVOFF_HOST_COHERENT
     case = H.build_case(sp, inputs, layers, reqs, host_kind=host_kind, two_regions=True)
+    kv.kvoff_set_attention_qk(case.ctx, kv.KVOFF_QK_VALU if args.attn_qk == "valu" else kv.KVOFF_QK_MFMA)
     if not keep_cpu:
         inputs.clear()
     else:  # only layer 0 is needed for the CPU baseline
@@ -424,7 +427,7 @@ def main():
             "workload": f"{sp.name}: batch {B}, {sp.Hq}/{sp.Hkv} heads, head_dim {sp.d}, "
                         f"context {reqs[0].ctx}, block {sp.bs}, top-{reqs[0].k}, "
                         f"{len(layers)} rotating layers",
-            "engine": args.engine, "host_mem": args.host_mem,
+            "engine": args.engine, "host_mem": args.host_mem, "attn_qk": args.attn_qk,
             "global_batch": B, "seq_len": reqs[0].ctx,
         },
         "roofline": {

@@ -100,6 +100,13 @@ enum {
   KVOFF_ENGINE_STAGED = 2
 };
 
+/* what runs the QK^T contraction of the attention (the G query heads of a
+   group against a block's keys) */
+enum {
+  KVOFF_QK_MFMA = 0, /* v_mfma_f32_16x16x32 on the matrix cores (default) */
+  KVOFF_QK_VALU = 1  /* v_dot2 on the vector ALUs; G <= 8 only          */
+};
+
 /* kind of pinned host memory for the store */
 enum {
   KVOFF_HOST_COHERENT = 0,   /* fine-grained (hipHostMallocCoherent)      */
@@ -151,6 +158,12 @@ int64_t kvoff_record_bytes(const kvoff_ctx* ctx);
 /* Sets lambda of KVOFF_CONSENSUS (>= 0; the guide prints 0.5 in its formula
  * and simulator and 1 in its worked figure).  Errors: EINVAL. */
 int kvoff_set_consensus_lambda(kvoff_ctx* ctx, double lambda);
+
+/* Chooses what computes the attention's QK^T (KVOFF_QK_MFMA or
+ * KVOFF_QK_VALU) for later kvoff_sparse_decode / kvoff_step calls on this
+ * context.  Both give the same result within fp32 rounding.  Errors: EINVAL
+ * (unknown value, or KVOFF_QK_VALU with G = Hq/Hkv > 8). */
+int kvoff_set_attention_qk(kvoff_ctx* ctx, int32_t qk);
 
 /* Reserves store capacity for a request of n_tokens tokens in every layer
  * (nb = ceil(n_tokens / bs) records per layer) and returns its id in

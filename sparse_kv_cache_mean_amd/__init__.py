@@ -24,6 +24,7 @@ KVOFF_OK = 0
 KVOFF_EINVAL, KVOFF_ENOMEM, KVOFF_ENODEV, KVOFF_EHIP, KVOFF_ERANGE, KVOFF_ESTATE = range(-1, -7, -1)
 KVOFF_F16, KVOFF_BF16 = 1, 2
 KVOFF_SOLOHEAD, KVOFF_HEADWISE, KVOFF_CONSENSUS = 0, 1, 2
+KVOFF_QK_MFMA, KVOFF_QK_VALU = 0, 1
 KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA, KVOFF_ENGINE_STAGED = 0, 1, 2
 KVOFF_HOST_COHERENT, KVOFF_HOST_NONCOHERENT = 0, 1
 KVOFF_CALL_SPARSE_DECODE, KVOFF_CALL_STEP = 1, 2
@@ -31,6 +32,7 @@ KVOFF_MAX_BATCH = 128
 
 EXPORTS = (
     "kvoff_create", "kvoff_destroy", "kvoff_record_bytes", "kvoff_set_consensus_lambda",
+    "kvoff_set_attention_qk",
     "kvoff_register_request",
     "kvoff_host_record", "kvoff_offload_blocks", "kvoff_select", "kvoff_recall",
     "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_read",
@@ -109,6 +111,7 @@ def lib() -> ctypes.CDLL:
     L.kvoff_record_bytes.restype = i64
     L.kvoff_register_request.argtypes = [_vp, i64, P(i32)]
     L.kvoff_set_consensus_lambda.argtypes = [_vp, ctypes.c_double]
+    L.kvoff_set_attention_qk.argtypes = [_vp, i32]
     L.kvoff_host_record.argtypes = [_vp, i32, i32, i64, P(_vp)]
     L.kvoff_offload_blocks.argtypes = [_vp, i32, i32, _vp, _vp, _vp, _vp]
     L.kvoff_select.argtypes = [_vp, i32, i32, _vp, _vp, _vp, i64, _vp, i32, _vp, _vp, _vp, i32, _vp]
@@ -130,7 +133,7 @@ def lib() -> ctypes.CDLL:
     L.kvoff_last_error.argtypes = []
     L.kvoff_last_error.restype = ctypes.c_char_p
     for name in ("kvoff_create", "kvoff_destroy", "kvoff_register_request", "kvoff_host_record",
-                 "kvoff_set_consensus_lambda",
+                 "kvoff_set_consensus_lambda", "kvoff_set_attention_qk",
                  "kvoff_offload_blocks", "kvoff_select", "kvoff_recall", "kvoff_sparse_decode",
                  "kvoff_step", "kvoff_probe_read", "kvoff_admission_plan", "kvoff_make_resident",
                  "kvoff_release_resident"):
@@ -193,6 +196,10 @@ def kvoff_record_bytes(ctx: int) -> int:
 
 def kvoff_set_consensus_lambda(ctx: int, lam: float) -> None:
     _check(lib().kvoff_set_consensus_lambda(ctx, lam))
+
+
+def kvoff_set_attention_qk(ctx: int, qk: int) -> None:
+    _check(lib().kvoff_set_attention_qk(ctx, qk))
 
 
 def kvoff_register_request(ctx: int, n_tokens: int) -> int:

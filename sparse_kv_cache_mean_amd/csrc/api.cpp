@@ -176,6 +176,15 @@ int kvoff_set_consensus_lambda(kvoff_ctx* ctx, double lambda) {
   return KVOFF_OK;
 }
 
+int kvoff_set_attention_qk(kvoff_ctx* ctx, int32_t qk) {
+  if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
+  if (qk != KVOFF_QK_MFMA && qk != KVOFF_QK_VALU) return fail(KVOFF_EINVAL, "unknown QK engine %d", qk);
+  if (qk == KVOFF_QK_VALU && ctx->G > 8)
+    return fail(KVOFF_EINVAL, "the VALU QK needs G <= 8 (G = %d)", ctx->G);
+  ctx->attn_qk = qk;
+  return KVOFF_OK;
+}
+
 int kvoff_register_request(kvoff_ctx* ctx, int64_t n_tokens, int32_t* req_id) {
   if (!ctx || !req_id) return fail(KVOFF_EINVAL, "ctx and req_id must be non-NULL");
   if (n_tokens < 1) return fail(KVOFF_EINVAL, "n_tokens %lld < 1", (long long)n_tokens);

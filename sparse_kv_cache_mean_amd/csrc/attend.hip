@@ -11,13 +11,19 @@
 // Design (split-K flash decoding, one workgroup per (request, KV head,
 // split), 4 waves, each wave an independent online-softmax worker over
 // `bpw` consecutive selected blocks):
-//   QK   v_mfma_f32_16x16x32_{bf16,f16}: A = 16 tokens x 32 dims of the K
-//        tile loaded straight from HBM (each lane 16 contiguous bytes, four
-//        lanes cover 64 contiguous bytes of a token row), B = the G query
-//        heads of the group (columns >= G are zero).  The result gives lane
-//        (quad, col) the logits of tokens quad*4..quad*4+3 for head col.
-//   softmax  running max / sum per head in the log2 domain, reduced across
-//        the four quads with lane shuffles; probabilities go to LDS.
+//   K tile  lane (quad, col) loads 16 contiguous bytes of token row
+//        t*16 + col at dims m*32 + quad*8 (m = 0..3), so four lanes cover 64
+//        contiguous bytes of a row.
+//   QK on the matrix cores (MFMA=true): v_mfma_f32_16x16x32_{bf16,f16} with
+//        A = that 16-token x 32-dim tile and B = the G query heads of the
+//        group (columns >= G are zero).  Lane (quad, col) gets the logits of
+//        tokens quad*4..quad*4+3 for head col; the running max / sum per head
+//        is reduced across the four quads with lane shuffles.
+//   QK on the vector ALUs (MFMA=false, G <= 8): v_dot2 over the same tile
+//        against the lane's 32 query dims of every head, summed across the
+//        four quads; every lane then holds all G heads' logits of its two
+//        tokens and the per-head max / sum are reduced across the 16 columns.
+//   softmax  log2 domain; probabilities go to LDS.
 //   PV   fp32 VALU: lane (token group quad, dim group col) loads 16 bytes of
 //        V rows t = quad + 4k and accumulates o[h][8 dims] for all G heads.
 // The four waves merge in LDS; one partial (m, l, o[128]) per (head, split)
@@ -38,6 +44,8 @@ constexpr int PART = 2 + kHeadDim;  // m, l, o[128]
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 
 struct AttendArgs {
   BatchIds batch;
@@ -85,22 +93,39 @@ __device__ __forceinline__ void unpack8(uint4 w, float f[8]) {
   }
 }
 
-template <typename T, bool NT>
-__device__ __forceinline__ T load16(const void* p) {
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
-  u32x4_t x;
-  if constexpr (NT)
-    x = __builtin_nontemporal_load(q);
-  else
-    x = *q;
-  return T{x[0], x[1], x[2], x[3]};
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// sum over lanes (a, b, 2 packed values each) of a * b, accumulated into c
+template <bool BF16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                  false);
+  }
 }
 
-template <int G, int BS, bool BF16, bool NT>
+template <int W>  // max / sum over the W lanes of an aligned group (W <= 16)
+__device__ __forceinline__ float row_max(float v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+template <int W>
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < W; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <int G, int BS, bool BF16, bool MFMA>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+  static_assert(MFMA || G <= 8, "the VALU QK keeps every head's query slice in registers");
   constexpr int D = kHeadDim;
   constexpr int TILES = BS / 16;
+  constexpr int GV = MFMA ? 1 : G;  // heads whose query slice a lane holds (VALU)
   __shared__ float p_s[ATT_WAVES][BS][G];
   __shared__ float alpha_s[ATT_WAVES][G];
   __shared__ float wm[ATT_WAVES][G], wl[ATT_WAVES][G];
@@ -119,14 +144,23 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   const int i0 = (s * ATT_WAVES + wave) * a.bpw;
   const int i1 = min(i0 + a.bpw, cnt);
 
-  // B fragments: query head g*G + col, dims m*32 + quad*8 .. +7
+  // MFMA: B fragments, query head g*G + col, dims m*32 + quad*8 .. +7.
+  // VALU: the same dims of every head of the group.
   uint4 qf[4];
-  {
+  uint4 qv[GV][4];
+  if constexpr (MFMA) {
     const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + min(col, G - 1)) * D;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       qf[m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
       if (col >= G) qf[m] = make_uint4(0, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < GV; ++h) {
+      const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) qv[h][m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
     }
   }
   // the wave's block ids and table entries, loaded once (at most 4 blocks)
@@ -139,7 +173,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     ent_w[k] = a.table[row + i];
   }
 
-  float m_run = -INFINITY, l_run = 0.f;  // head col's running max (log2) and sum
+  float m_run = -INFINITY, l_run = 0.f;  // MFMA: head col's running max (log2) and sum
+  float mh[GV], lh[GV];                  // VALU: every head's
+#pragma unroll
+  for (int h = 0; h < GV; ++h) {
+    mh[h] = -INFINITY;
+    lh[h] = 0.f;
+  }
   float o[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -162,55 +202,97 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        kf[t][m] = load16<uint4, NT>(Kp + (t * 16 + col) * D + m * 32 + quad * 8);
+        kf[t][m] = load16(Kp + (t * 16 + col) * D + m * 32 + quad * 8);
     uint4 vf[BS / 4];
 #pragma unroll
-    for (int k = 0; k < BS / 4; ++k)
-      vf[k] = load16<uint4, NT>(Vp + (quad + 4 * k) * D + col * 8);
+    for (int k = 0; k < BS / 4; ++k) vf[k] = load16(Vp + (quad + 4 * k) * D + col * 8);
 
-    float z[TILES][4];
+    if constexpr (MFMA) {
+      float z[TILES][4];
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < TILES; ++t) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc = mfma16x16x32<BF16>(kf[t][m], qf[m], acc);
+        for (int m = 0; m < 4; ++m) acc = mfma16x16x32<BF16>(kf[t][m], qf[m], acc);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = t * 16 + quad * 4 + v;
-        z[t][v] = tok < n_valid ? acc[v] * a.scale_log2 : -INFINITY;
+        for (int v = 0; v < 4; ++v) {
+          const int tok = t * 16 + quad * 4 + v;
+          z[t][v] = tok < n_valid ? acc[v] * a.scale_log2 : -INFINITY;
+        }
       }
-    }
-    float bm = -INFINITY;
+      float bm = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t)
+      for (int t = 0; t < TILES; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) bm = fmaxf(bm, z[t][v]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    const float alpha = exp2f(m_run - m_new);
-    float ps = 0.f;
-    wave_sync_lds();
+        for (int v = 0; v < 4; ++v) bm = fmaxf(bm, z[t][v]);
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m_run, bm);
+      const float alpha = exp2f(m_run - m_new);
+      float ps = 0.f;
+      wave_sync_lds();
 #pragma unroll
-    for (int t = 0; t < TILES; ++t)
+      for (int t = 0; t < TILES; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = exp2f(z[t][v] - m_new);
-        ps += p;
-        if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
+        for (int v = 0; v < 4; ++v) {
+          const float p = exp2f(z[t][v] - m_new);
+          ps += p;
+          if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
+      wave_sync_lds();
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float al = alpha_s[wave][h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] *= al;
       }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
-    wave_sync_lds();
-
+    } else {
+      // z[t][h]: logit of token t*16 + col for head h, partial over the
+      // lane's 32 dims, then summed across the four quads
+      float z[TILES][GV];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float al = alpha_s[wave][h];
+      for (int t = 0; t < TILES; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= al;
+        for (int h = 0; h < GV; ++h) {
+          float acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            acc = dot2<BF16>(kf[t][m].x, qv[h][m].x, acc);
+            acc = dot2<BF16>(kf[t][m].y, qv[h][m].y, acc);
+            acc = dot2<BF16>(kf[t][m].z, qv[h][m].z, acc);
+            acc = dot2<BF16>(kf[t][m].w, qv[h][m].w, acc);
+          }
+          acc += __shfl_xor(acc, 16);
+          acc += __shfl_xor(acc, 32);
+          z[t][h] = t * 16 + col < n_valid ? acc * a.scale_log2 : -INFINITY;
+        }
+      wave_sync_lds();
+#pragma unroll
+      for (int h = 0; h < GV; ++h) {
+        float bm = z[0][h];
+#pragma unroll
+        for (int t = 1; t < TILES; ++t) bm = fmaxf(bm, z[t][h]);
+        bm = row_max<16>(bm);
+        const float m_new = fmaxf(mh[h], bm);
+        const float alpha = exp2f(mh[h] - m_new);
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < TILES; ++t) {
+          const float p = exp2f(z[t][h] - m_new);
+          ps += p;
+          if ((h & 3) == quad) p_s[wave][t * 16 + col][h] = p;
+        }
+        lh[h] = lh[h] * alpha + row_sum<16>(ps);
+        mh[h] = m_new;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+      }
+      wave_sync_lds();
     }
 #pragma unroll
     for (int k = 0; k < BS / 4; ++k) {
@@ -239,9 +321,17 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e) wo[wave][h][col * 8 + e] = o[h][e];
-    if (col < G) {
-      wm[wave][col] = m_run;
-      wl[wave][col] = l_run;
+    if constexpr (MFMA) {
+      if (col < G) {
+        wm[wave][col] = m_run;
+        wl[wave][col] = l_run;
+      }
+    } else if (col == 0) {
+#pragma unroll
+      for (int h = 0; h < GV; ++h) {
+        wm[wave][h] = mh[h];
+        wl[wave][h] = lh[h];
+      }
     }
   }
   __syncthreads();
@@ -316,40 +406,28 @@ int attend_bpw(int32_t k_stride) {
   return k_stride <= 128 ? 2 : 4;
 }
 
-// K/V tile loads with the nontemporal hint only if KVOFF_ATT_NT=1.  Off by
-// default: the tiles were just written by the recall and are partly still
-// in L2 / the Infinity Cache, which the hint forgoes (measured 31.6 -> 38.8
-// us on the Llama-3-8B-shaped layer).
-bool attend_nt() {
-  static const bool v = [] {
-    const char* e = std::getenv("KVOFF_ATT_NT");
-    return e && e[0] == '1';
-  }();
-  return v;
-}
-
-template <int G, int BS, bool NT>
-void launch_g_bs_nt(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s) {
+template <int G, int BS, bool MFMA>
+void launch_g_bs_qk(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL((attend_kernel<G, BS, true, NT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<G, BS, true, MFMA>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attend_kernel<G, BS, false, NT>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_kernel<G, BS, false, MFMA>), grid, dim3(256), 0, s, a);
 }
 
 template <int G, int BS>
-void launch_g_bs(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s) {
-  if (attend_nt())
-    launch_g_bs_nt<G, BS, true>(a, bf16, grid, s);
-  else
-    launch_g_bs_nt<G, BS, false>(a, bf16, grid, s);
+void launch_g_bs(const AttendArgs& a, bool bf16, bool mfma, dim3 grid, hipStream_t s) {
+  if constexpr (G <= 8) {  // kvoff_set_attention_qk admits VALU only for G <= 8
+    if (!mfma) return launch_g_bs_qk<G, BS, false>(a, bf16, grid, s);
+  }
+  launch_g_bs_qk<G, BS, true>(a, bf16, grid, s);
 }
 
 template <int G>
-void launch_g(const AttendArgs& a, int bs, bool bf16, dim3 grid, hipStream_t s) {
+void launch_g(const AttendArgs& a, int bs, bool bf16, bool mfma, dim3 grid, hipStream_t s) {
   if (bs == 16)
-    launch_g_bs<G, 16>(a, bf16, grid, s);
+    launch_g_bs<G, 16>(a, bf16, mfma, grid, s);
   else
-    launch_g_bs<G, 32>(a, bf16, grid, s);
+    launch_g_bs<G, 32>(a, bf16, mfma, grid, s);
 }
 
 }  // namespace
@@ -387,12 +465,13 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   const dim3 grid((unsigned)(b.n * a.Hkv * a.S));
   const bool bf16 = ctx->cfg.dtype == KVOFF_BF16;
   const int bs = ctx->cfg.block_size;
+  const bool mfma = ctx->attn_qk == KVOFF_QK_MFMA;
   switch (ctx->G) {
-    case 1: launch_g<1>(a, bs, bf16, grid, stream); break;
-    case 2: launch_g<2>(a, bs, bf16, grid, stream); break;
-    case 4: launch_g<4>(a, bs, bf16, grid, stream); break;
-    case 8: launch_g<8>(a, bs, bf16, grid, stream); break;
-    default: launch_g<16>(a, bs, bf16, grid, stream); break;
+    case 1: launch_g<1>(a, bs, bf16, mfma, grid, stream); break;
+    case 2: launch_g<2>(a, bs, bf16, mfma, grid, stream); break;
+    case 4: launch_g<4>(a, bs, bf16, mfma, grid, stream); break;
+    case 8: launch_g<8>(a, bs, bf16, mfma, grid, stream); break;
+    default: launch_g<16>(a, bs, bf16, mfma, grid, stream); break;
   }
   KVOFF_HIP(hipGetLastError());
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,

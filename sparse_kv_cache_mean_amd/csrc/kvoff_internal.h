@@ -44,6 +44,7 @@ struct kvoff_ctx {
   int device = 0;
   int G = 1;
   double consensus_lambda = 0.5;  // KVOFF_CONSENSUS mode
+  int32_t attn_qk = KVOFF_QK_MFMA;  // what computes the attention's QK^T
   int64_t rec_bytes = 0;    // 2 * Hkv * bs * d * es
   int64_t slice_bytes = 0;  // 2 * bs * d * es (K and V of one KV head)
   uint8_t* store = nullptr; // pinned host store (mapped into the GPU's address space)

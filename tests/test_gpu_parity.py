@@ -151,6 +151,53 @@ def test_group_sizes(Hq, Hkv):
         H.destroy(c)
 
 
+@pytest.mark.parametrize("spec_args", [
+    dict(wl=1),                                              # fp16, bs 16, G 4
+    dict(wl=2, B=2, Hq=8, Hkv=8, ctx=2000, k=12, hot=5),     # bf16, bs 32, G 1
+    dict(wl=2, B=2, Hq=16, Hkv=8, ctx=2000, k=12, hot=5),    # G 2
+    dict(wl=4, B=4, ctx_range=(700, 5000)),                  # G 8, ragged contexts
+    dict(wl=5, B=2, ctx=4096, k=16, hot=6, headwise=True),   # G 4, headwise
+])
+def test_attention_qk_on_vector_alus(spec_args):
+    """The v_dot2 QK^T matches the oracle to the same bar as the MFMA one, in
+    SoloHead and headwise layouts, over ragged last blocks."""
+    args = dict(spec_args)
+    wl = args.pop("wl")
+    s = synth.spec(wl, **args)
+    H.log(f"[qk valu] {s.name} Hq {s.Hq} Hkv {s.Hkv} bs {s.bs}")
+    c, sl = _case(s, [0])
+    try:
+        modes = [kv.KVOFF_SOLOHEAD] + ([kv.KVOFF_HEADWISE] if s.headwise else [])
+        for mode in modes:
+            kv.kvoff_set_attention_qk(c.ctx, kv.KVOFF_QK_MFMA)
+            bufs = H.make_buffers(c, mode)
+            H.run_layer(c, 0, mode, bufs)
+            torch.cuda.synchronize()
+            mfma_out = bufs.out.cpu().numpy().copy()
+            kv.kvoff_set_attention_qk(c.ctx, kv.KVOFF_QK_VALU)
+            bufs.out.fill_(float("nan"))
+            H.run_layer(c, 0, mode, bufs)
+            torch.cuda.synchronize()
+            err = P.check_attention(c, 0, mode, bufs, sl)
+            H.log(f"  mode {mode} attention err {err} "
+                  f"max |valu - mfma| {np.abs(bufs.out.cpu().numpy() - mfma_out).max():.3g}")
+    finally:
+        H.destroy(c)
+
+
+def test_attention_qk_valu_rejects_large_groups():
+    s = synth.spec(2, B=1, Hq=32, Hkv=2, ctx=512, k=4, hot=1)
+    c, _ = _case(s, [0])
+    try:
+        with pytest.raises(kv.KvoffError) as e:
+            kv.kvoff_set_attention_qk(c.ctx, kv.KVOFF_QK_VALU)
+        assert e.value.status == kv.KVOFF_EINVAL
+        with pytest.raises(kv.KvoffError):
+            kv.kvoff_set_attention_qk(c.ctx, 7)
+    finally:
+        H.destroy(c)
+
+
 def test_degenerate_sizes():
     """k >= nb (take every block), k = 1, one-token and one-block contexts."""
     H.log("[degenerate]")
@@ -251,6 +298,58 @@ def test_step_request_groups_match_whole_batch(engine):
                 assert np.array_equal(results[grp][0][l].view(np.uint32),
                                       results[0][0][l].view(np.uint32)), (grp, l)
             assert results[grp][1]["items_recalled"] == results[0][1]["items_recalled"]
+        for l in layers:
+            P.check_attention_close(results[0][0][l], P.oracle_attention(c, l, mode, sl), f"layer {l}")
+    finally:
+        H.destroy(c)
+
+
+def test_step_groups_with_resident_requests():
+    """Request groups reordered by residency (resident groups first, a
+    different order per layer) still give the whole-batch bits, and pinned
+    (layer, request) pairs recall nothing."""
+    H.log("[step groups] resident requests")
+    s = RAGGED_LAYERS
+    layers = [0, 1]
+    reqs, sl = _slices(s, layers)
+    nb_tot = sum(rq.nb for rq in reqs)
+    c = H.build_case(s, {k: v.lr for k, v in sl.items()}, layers, reqs, extra_slots=2 * nb_tot)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        sets = [H.make_buffers(c, mode) for _ in range(2)]
+        compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+        hit = [torch.zeros((c.B, c.nb_max), dtype=torch.uint8, device="cuda") for _ in layers]
+        slot = [torch.full((c.B, c.nb_max), -1, dtype=torch.int32, device="cuda") for _ in layers]
+        pinned = {0: [4, 5], 1: [1, 3]}  # layer -> requests made resident
+        first = c.extra_base
+        for l, rs in pinned.items():
+            for r in rs:
+                kv.kvoff_make_resident(c.ctx, l, c.rids[r], c.pool, c.n_slots, first, hit[l][r],
+                                       slot[l][r])
+                first += reqs[r].nb
+        torch.cuda.synchronize()
+        results = {}
+        for grp in (0, 1, 2):
+            outs = [torch.full((c.B, s.Hq, s.d), float("nan"), device="cuda") for _ in layers]
+            st = kv.kvoff_step(
+                c.ctx, layer_begin=0, layer_end=2, req_ids=c.rids, topk=[rq.k for rq in reqs],
+                mode=mode, engine=kv.KVOFF_ENGINE_ZEROCOPY, k_stride=c.k_stride,
+                q=[c.q[l] for l in layers], digest=[c.digest[l] for l in layers],
+                digest_stride=c.nb_max, slot_pool=c.pool, n_slots=c.n_slots,
+                recall_base_slot=c.recall_base, scores=[b.scores for b in sets],
+                sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
+                block_table=[b.table for b in sets], scale=1.0 / math.sqrt(s.d), out=outs,
+                ws=sets[0].ws, pool_hit=hit, pool_slot=slot, pool_stride=c.nb_max,
+                compute_stream=compute, copy_stream=copy, want_stats=True, group_requests=grp)
+            torch.cuda.synchronize()
+            results[grp] = ([o.cpu().numpy() for o in outs], st)
+        want_items = sum(min(reqs[r].k, reqs[r].nb) for l in layers for r in range(c.B)
+                         if r not in pinned[l])
+        for grp in (0, 1, 2):
+            assert results[grp][1]["items_recalled"] == want_items, grp
+            for l in layers:
+                assert np.array_equal(results[grp][0][l].view(np.uint32),
+                                      results[0][0][l].view(np.uint32)), (grp, l)
         for l in layers:
             P.check_attention_close(results[0][0][l], P.oracle_attention(c, l, mode, sl), f"layer {l}")
     finally:
