@@ -77,10 +77,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-overlap", action="store_true",
                    help="skip the overlapped kvoff_step measurement (for clean kernel traces)")
-    p.add_argument("--report", choices=["fragmentation", "admission"], default=None,
-                   help="instead of the bench line: recall of the headwise-vs-SoloHead "
-                        "workload (per-KV-head vs shared block sets, 25%% pool hits) with "
-                        "both engines: transfers, mean transfer size, GB/s")
+    p.add_argument("--report", choices=["fragmentation", "admission", "groups"], default=None,
+                   help="instead of the bench line: fragmentation = recall of the "
+                        "headwise-vs-SoloHead workload with every engine; admission = the "
+                        "multi-layer step before and after one admission decision; groups = "
+                        "interruptible per-request scheduling on the variable-recall layer")
     return p.parse_args()
 
 
@@ -291,6 +292,65 @@ def admission_report(args):
     print(json.dumps(out), flush=True)
 
 
+def groups_report(args):
+    """Interruptible per-request scheduling on the variable-recall layer
+    (batch 32, contexts 8K-128K, top-k 2-15%): the same kvoff_step with the
+    whole batch as one group and with smaller request groups, optionally
+    with a quarter of the requests pinned in HBM.  Reports the compute
+    stream's wait for recalls and when requests finish."""
+    sp = synth.spec(4)
+    reqs = synth.request_draws(sp)
+    B = len(reqs)
+    n_pin = B // 4
+    extra = sum(rq.nb for rq in reqs[:n_pin])
+    log(f"generating '{sp.name}' ({B} requests)")
+    case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                        [0], reqs, keep=lambda l, r: False, extra_slots=extra)
+    mode, engine = kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY
+    sets = [H.make_buffers(case, mode) for _ in range(2)]
+    out = [torch.empty_like(sets[0].out)]
+    hit = [torch.zeros((B, case.nb_max), dtype=torch.uint8, device="cuda")]
+    slot = [torch.full((B, case.nb_max), -1, dtype=torch.int32, device="cuda")]
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    topk = [rq.k for rq in reqs]
+
+    def step(grp, want_stats=False):
+        return kv.kvoff_step(
+            case.ctx, layer_begin=0, layer_end=1, req_ids=case.rids, topk=topk, mode=mode,
+            engine=engine, k_stride=case.k_stride, q=[case.q[0]], digest=[case.digest[0]],
+            digest_stride=case.nb_max, slot_pool=case.pool, n_slots=case.n_slots,
+            recall_base_slot=case.recall_base, scores=[b.scores for b in sets],
+            sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
+            block_table=[b.table for b in sets], scale=1.0 / math.sqrt(sp.d), out=out,
+            ws=sets[0].ws, pool_hit=hit, pool_slot=slot, pool_stride=case.nb_max,
+            compute_stream=compute, copy_stream=copy, want_stats=want_stats,
+            group_requests=grp, want_timing=True)
+
+    def measure(grp, n=5):
+        first = step(grp, want_stats=True)
+        ts = [step(grp)["timing"] for _ in range(n)]
+        res = {k: round(float(np.mean([t[k] for t in ts])), 4) for k in ts[0]}
+        res["group_requests"] = grp
+        res["recalled_bytes"] = first["bytes"]
+        log(str(res))
+        return res
+
+    runs = [measure(g) for g in (0, 16, 8, 4, 1)]
+    first = case.extra_base
+    for r in range(n_pin):
+        kv.kvoff_make_resident(case.ctx, 0, case.rids[r], case.pool, case.n_slots, first,
+                               hit[0][r], slot[0][r])
+        first += reqs[r].nb
+    torch.cuda.synchronize()
+    pinned = [measure(g) for g in (0, 8, 1)]
+    res = {"workload": f"{sp.name}: batch {B}, {sp.Hq}/{sp.Hkv} heads, contexts "
+                       f"{min(rq.ctx for rq in reqs)}-{max(rq.ctx for rq in reqs)}, top-k "
+                       f"{min(topk)}-{max(topk)} blocks, one layer, zero-copy recall",
+           "groups": runs, "with_first_quarter_resident": pinned}
+    H.destroy(case)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -304,6 +364,8 @@ def main():
         return fragmentation_report(args)
     if args.report == "admission":
         return admission_report(args)
+    if args.report == "groups":
+        return groups_report(args)
     sp = synth.spec(args.config, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)

@@ -305,11 +305,26 @@ typedef struct kvoff_step_args {
      Scheduling"): the batch is cut into contiguous groups of n requests,
      each group's recall is followed on the compute stream by that group's
      attention as soon as its own recall has landed, so attention of early
-     groups runs while later groups are still crossing the link.  Groups go
-     in ascending order of their selected-block count (fewest first).
+     groups runs while later groups are still crossing the link.  Within a
+     layer the groups go in ascending order of the blocks they must
+     transfer: the selected blocks of their requests that kvoff_make_resident
+     has not pinned for that layer (fewest first, ties in batch order).
      Outputs are identical to n = 0. */
   int32_t group_requests;
+  /* nullable host pointer: when set, the step records timing events on the
+     compute stream and, after synchronising it, fills *timing */
+  struct kvoff_step_timing* timing;
 } kvoff_step_args;
+
+/* Where the compute stream's time went in one kvoff_step, from HIP timing
+ * events on that stream (milliseconds). */
+typedef struct kvoff_step_timing {
+  double step_ms;              /* first select launched -> last attention done */
+  double compute_wait_ms;      /* compute stream idle, waiting for recalls      */
+  double mean_request_done_ms; /* mean over requests of step start -> the end
+                                  of that request's last-layer attention       */
+  double max_request_done_ms;  /* the same, latest request                     */
+} kvoff_step_timing;
 
 int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* args);
 

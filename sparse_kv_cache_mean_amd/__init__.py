@@ -88,8 +88,17 @@ class kvoff_step_args(ctypes.Structure):
         ("scale", ctypes.c_float), ("out_dev", _vp),
         ("ws_dev", _vp), ("ws_bytes", ctypes.c_size_t),
         ("compute_stream", _vp), ("copy_stream", _vp), ("stats", _vp),
-        ("group_requests", ctypes.c_int32),
+        ("group_requests", ctypes.c_int32), ("timing", _vp),
     ]
+
+
+class kvoff_step_timing(ctypes.Structure):
+    _fields_ = [("step_ms", ctypes.c_double), ("compute_wait_ms", ctypes.c_double),
+                ("mean_request_done_ms", ctypes.c_double),
+                ("max_request_done_ms", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {k: float(getattr(self, k)) for k, _ in self._fields_}
 
 
 _lib = None
@@ -263,7 +272,10 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
                sel_cnt: Sequence, block_table: Sequence, scale: float, out: Sequence, ws,
                pool_hit: Optional[Sequence] = None, pool_slot: Optional[Sequence] = None,
                pool_stride: int = 0, compute_stream=None, copy_stream=None,
-               want_stats: bool = False, group_requests: int = 0) -> Optional[dict]:
+               want_stats: bool = False, group_requests: int = 0,
+               want_timing: bool = False) -> Optional[dict]:
+    """Returns None, or the summed kvoff_stats fields (want_stats) and/or
+    the compute-stream timing under "timing" (want_timing)."""
     n_layers = layer_end - layer_begin
     ids, tk = _i32_array(req_ids), _i32_array(topk)
     arr = lambda ts: (_vp * max(n_layers, 1))(*[_ptr(t) for t in ts])
@@ -299,8 +311,15 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
     st = kvoff_stats() if want_stats else None
     a.stats = ctypes.cast(ctypes.pointer(st), _vp) if st is not None else None
     a.group_requests = group_requests
+    tm = kvoff_step_timing() if want_timing else None
+    a.timing = ctypes.cast(ctypes.pointer(tm), _vp) if tm is not None else None
     _check(lib().kvoff_step(ctx, ctypes.byref(a)))
-    return st.as_dict() if st is not None else None
+    if st is None and tm is None:
+        return None
+    res = st.as_dict() if st is not None else {}
+    if tm is not None:
+        res["timing"] = tm.as_dict()
+    return res
 
 
 def kvoff_probe_read(ptr, n_bytes: int, sink, n_wg: int = 0, stream=None) -> None:

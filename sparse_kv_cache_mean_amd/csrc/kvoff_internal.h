@@ -65,6 +65,7 @@ struct kvoff_ctx {
   size_t table_cap = 0;
   hipEvent_t ev_stage = nullptr;            // behind the last staged copy
   std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
+  std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
   bool ev_stage_pending = false;
 };
 

@@ -36,6 +36,7 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     return fail(KVOFF_ERANGE, "layers [%d, %d) outside [0, %d)", A->layer_begin, A->layer_end,
                 ctx->cfg.num_layers);
   if (A->stats) memset(A->stats, 0, sizeof *A->stats);
+  if (A->timing) memset(A->timing, 0, sizeof *A->timing);
   if (L == 0 || A->n_req == 0) return KVOFF_OK;
   if (!A->q_dev || !A->digest_dev || !A->out_dev || !A->req_ids || !A->topk)
     return fail(KVOFF_EINVAL, "q_dev, digest_dev, out_dev, req_ids and topk must be non-NULL");
@@ -93,6 +94,17 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     KVOFF_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     ctx->ev_group.push_back(e);
   }
+  // timing events (on request): the step's start, then per (layer, group)
+  // before the wait for its recall, after it, and after its attention
+  const size_t NG = groups.size();
+  auto tev = [&](int li, size_t gi, int k) { return ctx->ev_timing[1 + ((size_t)li * NG + gi) * 3 + k]; };
+  if (A->timing) {
+    while (ctx->ev_timing.size() < 1 + 3 * (size_t)L * NG) {
+      hipEvent_t e;
+      KVOFF_HIP(hipEventCreate(&e));
+      ctx->ev_timing.push_back(e);
+    }
+  }
   const int sets = A->mode == KVOFF_HEADWISE ? ctx->cfg.num_kv_heads : 1;
   const int64_t q_row = (int64_t)ctx->cfg.num_q_heads * ctx->cfg.head_dim;  // elements per request
 
@@ -128,7 +140,9 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     for (int gi : order_for(li)) {
       const Group& g = groups[gi];
       const int64_t sel_off = (int64_t)g.r0 * sets * A->k_stride;
+      if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 0), cs));
       KVOFF_HIP(hipStreamWaitEvent(cs, ctx->ev_group[buf * groups.size() + gi], 0));
+      if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 1), cs));
       int st = kvoff_sparse_decode(
           ctx, g.n, A->req_ids + g.r0, A->mode,
           (const uint8_t*)A->q_dev[li] + g.r0 * q_row * 2, A->slot_pool_dev,
@@ -136,15 +150,33 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
           A->sel_cnt_dev[buf] + g.r0, A->k_stride, A->scale, A->out_dev[li] + g.r0 * q_row,
           A->ws_dev, A->ws_bytes, cs);
       if (st) return st;
+      if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 2), cs));
     }
     return KVOFF_OK;
   };
 
   int st;
+  if (A->timing) KVOFF_HIP(hipEventRecord(ctx->ev_timing[0], cs));
   if ((st = select_l(0)) || (st = recall_l(0))) return st;
   for (int li = 0; li < L; ++li) {
     if (li + 1 < L && ((st = select_l(li + 1)) || (st = recall_l(li + 1)))) return st;
     if ((st = attend_l(li))) return st;
+  }
+  if (A->timing) {
+    KVOFF_HIP(hipStreamSynchronize(cs));
+    kvoff_step_timing& T = *A->timing;
+    float ms;
+    for (int li = 0; li < L; ++li)
+      for (size_t gi = 0; gi < NG; ++gi) {
+        KVOFF_HIP(hipEventElapsedTime(&ms, tev(li, gi, 0), tev(li, gi, 1)));
+        T.compute_wait_ms += ms;
+      }
+    for (size_t gi = 0; gi < NG; ++gi) {  // requests finish with their last layer
+      KVOFF_HIP(hipEventElapsedTime(&ms, ctx->ev_timing[0], tev(L - 1, gi, 2)));
+      T.mean_request_done_ms += (double)ms * groups[gi].n / A->n_req;
+      T.max_request_done_ms = std::max(T.max_request_done_ms, (double)ms);
+    }
+    T.step_ms = T.max_request_done_ms;
   }
   return KVOFF_OK;
 }

@@ -340,9 +340,16 @@ def test_step_groups_with_resident_requests():
                 sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
                 block_table=[b.table for b in sets], scale=1.0 / math.sqrt(s.d), out=outs,
                 ws=sets[0].ws, pool_hit=hit, pool_slot=slot, pool_stride=c.nb_max,
-                compute_stream=compute, copy_stream=copy, want_stats=True, group_requests=grp)
+                compute_stream=compute, copy_stream=copy, want_stats=True, group_requests=grp,
+                want_timing=True)
             torch.cuda.synchronize()
             results[grp] = ([o.cpu().numpy() for o in outs], st)
+            t = st["timing"]
+            H.log(f"  groups of {grp}: {t}")
+            assert 0 < t["mean_request_done_ms"] <= t["max_request_done_ms"] == t["step_ms"]
+            assert 0 <= t["compute_wait_ms"] < t["step_ms"]
+            if grp == 0:
+                assert t["mean_request_done_ms"] == t["max_request_done_ms"]
         want_items = sum(min(reqs[r].k, reqs[r].nb) for l in layers for r in range(c.B)
                          if r not in pinned[l])
         for grp in (0, 1, 2):
