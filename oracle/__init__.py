@@ -52,6 +52,9 @@ def lib():
         L.oracle_score.argtypes = [vp, ci, ci, ci, ci, vp, i64, vp]
         L.oracle_score_headwise.argtypes = [vp, ci, ci, ci, ci, vp, i64, vp]
         L.oracle_score_consensus.argtypes = [vp, ci, ci, ci, ci, vp, i64, ctypes.c_double, vp]
+        L.oracle_score_group_consensus.argtypes = [vp, ci, ci, ci, ci, vp, i64, ctypes.c_double,
+                                                    vp]
+        L.oracle_attention_mass.argtypes = [vp, vp, ci, i64, ci, ci, ci, ci, vp, vp, ci, i64, vp]
         L.oracle_select.argtypes = [vp, i64, i64, vp]
         L.oracle_select.restype = i64
         L.oracle_records.argtypes = [vp, vp, i64, ci, ci, ci, vp]
@@ -128,6 +131,34 @@ def score_consensus(q: np.ndarray, dtype: int, D: np.ndarray, lam: float) -> np.
     S = np.empty(nb, np.float64)
     lib().oracle_score_consensus(_p(q), dtype, Hq, Hkv, d, _p(D), nb, lam, _p(S))
     return S
+
+
+def score_group_consensus(q: np.ndarray, dtype: int, D: np.ndarray, lam: float) -> np.ndarray:
+    """-> [Hkv][nb] per-GQA-group consensus scores."""
+    q = _u16(q)
+    D = np.ascontiguousarray(D, dtype=np.float32)
+    Hq, d = q.shape
+    nb, Hkv, _ = D.shape
+    S = np.empty((Hkv, nb), np.float64)
+    lib().oracle_score_group_consensus(_p(q), dtype, Hq, Hkv, d, _p(D), nb, lam, _p(S))
+    return S
+
+
+def attention_mass(q, K, dtype: int, bs: int, sel, counts=None) -> np.ndarray:
+    """sel: [K] shared by every head, or [Hkv][stride] per KV head (counts
+    entries each; default: the full rows).  -> mass [Hq] float64."""
+    q, K = _u16(q), _u16(K)
+    Hq, d = q.shape
+    ctx, Hkv, _ = K.shape
+    s = np.ascontiguousarray(sel, dtype=np.int32)
+    if s.ndim == 1:
+        s = s[None, :]
+    nsets, stride = s.shape
+    c = np.full(nsets, stride, np.int64) if counts is None else np.ascontiguousarray(counts, np.int64)
+    out = np.empty(Hq, np.float64)
+    lib().oracle_attention_mass(_p(q), _p(K), dtype, ctx, Hq, Hkv, d, bs, _p(s), _p(c), nsets,
+                                stride, _p(out))
+    return out
 
 
 def select(S: np.ndarray, k: int) -> np.ndarray:

@@ -103,6 +103,24 @@ void oracle_score_consensus(const uint16_t* q, int dtype, int Hq, int Hkv, int d
   free(Sg);
 }
 
+void oracle_score_group_consensus(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
+                                  const float* D, int64_t nb, double lambda, double* S) {
+  int G = Hq / Hkv;
+  for (int g = 0; g < Hkv; ++g) {
+    for (int64_t b = 0; b < nb; ++b) {
+      double mx = -INFINITY, sum = 0.0;
+      for (int h = g * G; h < (g + 1) * G; ++h) {
+        double s = 0.0;
+        for (int j = 0; j < d; ++j)
+          s += oracle_widen(q[h * d + j], dtype) * (double)D[(b * Hkv + g) * d + j];
+        if (s > mx) mx = s;
+        sum += s;
+      }
+      S[g * nb + b] = mx + lambda * (sum / (double)G);
+    }
+  }
+}
+
 /* ---------------------------------------------------------------- select */
 
 typedef struct {
@@ -344,4 +362,37 @@ void oracle_dense_f64(const uint16_t* q, const uint16_t* K, const uint16_t* V, i
     }
   }
   free(w);
+}
+
+void oracle_attention_mass(const uint16_t* q, const uint16_t* K, int dtype, int64_t ctx, int Hq,
+                           int Hkv, int d, int bs, const int32_t* sel, const int64_t* counts,
+                           int nsets, int64_t stride, double* mass) {
+  int G = Hq / Hkv;
+  int64_t nb = (ctx + bs - 1) / bs;
+  double* z = (double*)malloc((size_t)(ctx > 0 ? ctx : 1) * sizeof(double));
+  uint8_t* chosen = (uint8_t*)malloc((size_t)(nb > 0 ? nb : 1));
+  double scale = 1.0 / sqrt((double)d);
+  for (int h = 0; h < Hq; ++h) {
+    int g = h / G;
+    int set = nsets == 1 ? 0 : g;
+    for (int64_t b = 0; b < nb; ++b) chosen[b] = 0;
+    for (int64_t i = 0; i < counts[set]; ++i) chosen[sel[set * stride + i]] = 1;
+    double m = -INFINITY;
+    for (int64_t t = 0; t < ctx; ++t) {
+      double s = 0.0;
+      for (int j = 0; j < d; ++j)
+        s += oracle_widen(q[h * d + j], dtype) * oracle_widen(K[(t * Hkv + g) * d + j], dtype);
+      z[t] = s * scale;
+      if (z[t] > m) m = z[t];
+    }
+    double all = 0.0, kept = 0.0;
+    for (int64_t t = 0; t < ctx; ++t) {
+      double w = exp(z[t] - m);
+      all += w;
+      if (chosen[t / bs]) kept += w;
+    }
+    mass[h] = kept / all;
+  }
+  free(chosen);
+  free(z);
 }

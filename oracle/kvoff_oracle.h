@@ -79,6 +79,15 @@ void oracle_score_headwise(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
 void oracle_score_consensus(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
                             const float* D, int64_t nb, double lambda, double* S);
 
+/* Consensus score within each GQA group, the scope the guide's text gives
+ * ("PulseInfer Guide", aiFetchly, section "SoloHead Sparse Selection":
+ * consensus taken over the query heads of a GQA group):
+ *   S[g][b] = max_{h in g} s_h[b] + lambda * (sum_{h in g} s_h[b]) / G,
+ *   s_h[b]  = sum_j q[h][j] * D[b][g][j]  (the per-query-head score).
+ * One ranking per KV head, as in the headwise layout.  S is [Hkv][nb]. */
+void oracle_score_group_consensus(const uint16_t* q, int dtype, int Hq, int Hkv, int d,
+                                  const float* D, int64_t nb, double lambda, double* S);
+
 /* Top-k selection over nb scores: sel receives K = min(k, nb) block ids in
  * ascending order; returns K, or -1 if k < 1. */
 int64_t oracle_select(const double* S, int64_t nb, int64_t k, int32_t* sel);
@@ -121,6 +130,18 @@ void oracle_attend_f64(const uint16_t* q, const uint16_t* K, const uint16_t* V, 
 void oracle_attend_headwise_f32(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                                 int dtype, int64_t ctx, int Hq, int Hkv, int d, int bs,
                                 const int32_t* sel, int64_t nsel, int64_t stride, float* out);
+
+/* Attention mass a selection keeps (the quantity behind the guide's
+ * "attention mass preserved" figure, section "SoloHead Sparse Selection"):
+ * for each query head h, with fp64 logits z_t = <q_h, K_t[g]> / sqrt(d) over
+ * all ctx tokens and w_t = exp(z_t - max z),
+ *   mass[h] = (sum of w_t over the valid tokens of the blocks KV head
+ *              g = floor(h/G) selected) / (sum of w_t over all tokens).
+ * sel is [nsets][stride] with counts[s] entries in set s; nsets is 1 (one
+ * set shared by every head) or Hkv (one set per KV head). */
+void oracle_attention_mass(const uint16_t* q, const uint16_t* K, int dtype, int64_t ctx, int Hq,
+                           int Hkv, int d, int bs, const int32_t* sel, const int64_t* counts,
+                           int nsets, int64_t stride, double* mass);
 
 /* Dense decode attention in fp64 over all ctx tokens, by token index alone
  * (no block bookkeeping): the textbook definition. */

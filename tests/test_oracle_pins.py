@@ -432,3 +432,84 @@ def test_consensus_bruteforce_and_special_cases():
     D1 = rng.standard_normal((nb, 1, d)).astype(np.float32)
     assert np.allclose(oracle.score_consensus(q1, BF16, D1, 0.5), 1.5 * oracle.score(q1, BF16, D1),
                        rtol=1e-14, atol=0)
+
+
+def test_group_consensus_bruteforce_and_special_cases():
+    """Consensus within each GQA group: exact rational brute force; lambda = 0
+    is the max over the group's query heads; the lambda term is the headwise
+    score / G; a group of identical heads gives (1 + lambda) * their score."""
+    rng = np.random.default_rng(33)
+    Hq, Hkv, d, nb = 8, 2, 8, 5
+    G = Hq // Hkv
+    q = _rand_bits(rng, (Hq, d), BF16)
+    D = rng.standard_normal((nb, Hkv, d)).astype(np.float32)
+    qv = _vals(q, BF16)
+    for lam in (0.0, 0.5, 1.0):
+        S = oracle.score_group_consensus(q, BF16, D, lam)
+        assert S.shape == (Hkv, nb)
+        for g in range(Hkv):
+            for b in range(nb):
+                per = [sum(Fraction(float(qv[h, j])) * Fraction(float(D[b, g, j])) for j in range(d))
+                       for h in range(g * G, (g + 1) * G)]
+                exact = max(per) + Fraction(lam) * sum(per) / G
+                assert abs(Fraction(S[g, b]) - exact) <= Fraction(1e-12) * (1 + abs(exact))
+    S0, S1 = oracle.score_group_consensus(q, BF16, D, 0.0), oracle.score_group_consensus(q, BF16, D, 1.0)
+    assert np.allclose((S1 - S0) * G, oracle.score_headwise(q, BF16, D), rtol=1e-12, atol=1e-12)
+    qs = q.copy()
+    for g in range(Hkv):
+        qs[g * G:(g + 1) * G] = q[g * G]
+    Sh = oracle.score_headwise(qs, BF16, D)
+    assert np.allclose(oracle.score_group_consensus(qs, BF16, D, 0.5), 1.5 * Sh / G, rtol=1e-13, atol=1e-13)
+
+
+def _softmax_mass_scipy(q, K, dtype, bs, sets):
+    """Independent form: logits by a numpy matmul, softmax by scipy, summed
+    over the selected tokens of each head's set."""
+    from scipy.special import softmax
+    Hq, d = q.shape
+    ctx, Hkv, _ = K.shape
+    G = Hq // Hkv
+    qv, Kv = _vals(q, dtype), _vals(K, dtype)
+    out = np.empty(Hq)
+    for h in range(Hq):
+        g = h // G
+        p = softmax((Kv[:, g, :] @ qv[h]) / np.sqrt(d))
+        chosen = np.isin(np.arange(ctx) // bs, sets[0 if len(sets) == 1 else g])
+        out[h] = p[chosen].sum()
+    return out
+
+
+def test_attention_mass_vs_scipy_softmax():
+    q, K, _ = _small_case(41, ctx=61)  # bs 8: last block holds 5 tokens
+    shared = np.array([0, 3, 7], np.int32)
+    m = oracle.attention_mass(q, K, BF16, 8, shared)
+    assert np.allclose(m, _softmax_mass_scipy(q, K, BF16, 8, [shared]), rtol=0, atol=1e-12)
+    per = np.array([[1, 2, 7], [0, 4, 6]], np.int32)
+    m = oracle.attention_mass(q, K, BF16, 8, per)
+    assert np.allclose(m, _softmax_mass_scipy(q, K, BF16, 8, list(per)), rtol=0, atol=1e-12)
+    # per-KV-head sets with equal rows are the shared set
+    assert np.array_equal(oracle.attention_mass(q, K, BF16, 8, np.stack([shared, shared])),
+                          oracle.attention_mass(q, K, BF16, 8, shared))
+
+
+def test_attention_mass_complement_and_mixture_identity():
+    """mass(S) + mass(complement) = 1, and the dense output is the mass-weighted
+    mix of the sparse outputs over S and its complement (ties the mass to the
+    attention oracle, itself pinned to torch's SDPA)."""
+    q, K, V = _small_case(42, ctx=70)  # 9 blocks of 8, the last holds 6 tokens
+    nb = 9
+    S = np.array([1, 2, 5, 8], np.int32)
+    C = np.setdiff1d(np.arange(nb, dtype=np.int32), S)
+    mS = oracle.attention_mass(q, K, BF16, 8, S)
+    mC = oracle.attention_mass(q, K, BF16, 8, C)
+    assert np.allclose(mS + mC, 1.0, rtol=0, atol=1e-12)
+    assert np.all((mS > 0) & (mS < 1))
+    mix = mS[:, None] * oracle.attend_f64(q, K, V, BF16, 8, S) + \
+        mC[:, None] * oracle.attend_f64(q, K, V, BF16, 8, C)
+    assert np.allclose(mix, oracle.dense_f64(q, K, V, BF16), rtol=0, atol=1e-12)
+    # every block selected keeps all of the mass; counts limit the set
+    assert np.array_equal(oracle.attention_mass(q, K, BF16, 8, np.arange(nb, dtype=np.int32)),
+                          np.ones(q.shape[0]))
+    assert np.array_equal(oracle.attention_mass(q, K, BF16, 8, np.array([[1, 2, 5, 8]], np.int32),
+                                                counts=[2]),
+                          oracle.attention_mass(q, K, BF16, 8, np.array([1, 2], np.int32)))
