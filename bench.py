@@ -77,11 +77,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-overlap", action="store_true",
                    help="skip the overlapped kvoff_step measurement (for clean kernel traces)")
-    p.add_argument("--report", choices=["fragmentation", "admission", "groups"], default=None,
+    p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass"], default=None,
                    help="instead of the bench line: fragmentation = recall of the "
                         "headwise-vs-SoloHead workload with every engine; admission = the "
                         "multi-layer step before and after one admission decision; groups = "
-                        "interruptible per-request scheduling on the variable-recall layer")
+                        "interruptible per-request scheduling on the variable-recall layer; "
+                        "mass = attention mass kept and recall volume of every selection mode")
     return p.parse_args()
 
 
@@ -351,6 +352,63 @@ def groups_report(args):
     print(json.dumps(res), flush=True)
 
 
+def mass_report(args):
+    """Attention mass kept and recall volume of every selection mode on the
+    headwise-vs-SoloHead shapes (batch 16, 32/8 heads, context 32768, top-64
+    blocks per set; no pool hits): the guide's claim is that one shared set
+    keeps nearly all the mass of per-head sets at a fraction of the volume."""
+    sp = synth.spec(5, pool_frac=0.0)
+    reqs = synth.request_draws(sp)
+    B = len(reqs)
+    log(f"generating '{sp.name}' ({B} requests)")
+    case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                        [0], reqs, keep=lambda l, r: False)
+    scale = 1.0 / math.sqrt(sp.d)
+    topk = [rq.k for rq in reqs]
+    rec = kv.kvoff_record_bytes(case.ctx)
+    runs = []
+    modes = [("solohead", kv.KVOFF_SOLOHEAD, None), ("consensus", kv.KVOFF_CONSENSUS, 0.5),
+             ("consensus", kv.KVOFF_CONSENSUS, 1.0), ("group_consensus", kv.KVOFF_CONSENSUS_GROUP, 0.5),
+             ("group_consensus", kv.KVOFF_CONSENSUS_GROUP, 1.0), ("headwise", kv.KVOFF_HEADWISE, None)]
+    for name, mode, lam in modes:
+        if lam is not None:
+            kv.kvoff_set_consensus_lambda(case.ctx, lam)
+        bufs = H.make_buffers(case, mode)
+        kv.kvoff_select(case.ctx, 0, case.rids, case.q[0], case.digest[0], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+        mass = torch.empty((B, sp.Hq), dtype=torch.float64, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kv.kvoff_attention_mass(case.ctx, 0, case.rids, mode, case.q[0], bufs.sel_idx,
+                                bufs.sel_cnt, case.k_stride, scale, mass)
+        e1.record()
+        st = kv.kvoff_recall(case.ctx, 0, case.rids, mode, bufs.sel_idx, bufs.sel_cnt,
+                             case.k_stride, None, None, 0, case.pool, case.n_slots,
+                             case.recall_base[0], bufs.table, kv.KVOFF_ENGINE_ZEROCOPY,
+                             want_stats=True)
+        torch.cuda.synchronize()
+        sel = bufs.sel_idx.cpu().numpy()
+        cnt = bufs.sel_cnt.cpu().numpy()
+        distinct = sum(len(np.unique(sel[r][:, :cnt[r]])) for r in range(B))
+        m = mass.cpu().numpy()
+        res = {"mode": name, "lambda": lam, "mean_mass": round(float(m.mean()), 5),
+               "min_head_mass": round(float(m.min()), 5), "recalled_bytes": st["bytes"],
+               "transfers": st["transfers"], "distinct_blocks": int(distinct),
+               "mass_kernel_ms": round(e0.elapsed_time(e1), 3)}
+        log(str(res))
+        runs.append(res)
+    hw = runs[-1]
+    for r in runs:
+        r["mass_vs_headwise"] = round(r["mean_mass"] / hw["mean_mass"], 4)
+        r["volume_vs_headwise"] = round(r["recalled_bytes"] / hw["recalled_bytes"], 4)
+    K_bytes = sum(rq.nb for rq in reqs) * sp.Hkv * sp.bs * sp.d * sp.es
+    res = {"workload": f"{sp.name} shapes: batch {B}, {sp.Hq}/{sp.Hkv} heads, context "
+                       f"{reqs[0].ctx}, block {sp.bs}, top-{reqs[0].k} per set, no pool hits",
+           "record_bytes": rec, "mass_kernel_reads_bytes": K_bytes, "runs": runs}
+    H.destroy(case)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -366,6 +424,8 @@ def main():
         return admission_report(args)
     if args.report == "groups":
         return groups_report(args)
+    if args.report == "mass":
+        return mass_report(args)
     sp = synth.spec(args.config, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)

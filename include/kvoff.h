@@ -76,7 +76,13 @@ enum {
      S_g[b], S_g the per-KV-head score; lambda per context (default 0.5).
      Its selection, recall and attention use the SoloHead layouts, and
      kvoff_recall / kvoff_sparse_decode treat it as KVOFF_SOLOHEAD. */
-  KVOFF_CONSENSUS = 2
+  KVOFF_CONSENSUS = 2,
+  /* the same consensus rule with the scope the guide's text gives: the query
+     heads of one GQA group.  S_g[b] = max_{h in g} s_h[b] + lambda *
+     mean_{h in g} s_h[b], s_h[b] = sum_j q[h][j] * D[b][g][j]; one set per
+     KV head, so it uses the KVOFF_HEADWISE layouts, and kvoff_recall /
+     kvoff_sparse_decode treat it as KVOFF_HEADWISE. */
+  KVOFF_CONSENSUS_GROUP = 3
 };
 
 /* recall engines */
@@ -327,6 +333,28 @@ typedef struct kvoff_step_timing {
 } kvoff_step_timing;
 
 int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* args);
+
+/* ------------------------------------------------------------- diagnostics of the selection */
+
+/* Attention mass a selection keeps ("PulseInfer Guide", aiFetchly, section
+ * "SoloHead Sparse Selection", attention mass preservation).  For request
+ * i and query head h (KV head g = floor(h/G)), with z_t = scale * <q_h,
+ * K_t[g]> over every valid token t of layer `layer` of the request:
+ *   mass_dev[i*Hq + h] = sum_{t in blocks selected for g} exp(z_t - max z)
+ *                        / sum_{all t} exp(z_t - max z).
+ * Logits in fp32, sums in fp64.  The keys are read from the pinned store
+ * over the host link (half of every record of the layer), so the call costs
+ * about as much as recalling the whole layer; it is a diagnostic, not part
+ * of the decode step.  mode: the layout of sel_idx_dev as kvoff_select wrote
+ * it (shared set for KVOFF_SOLOHEAD / KVOFF_CONSENSUS, one set per KV head
+ * for KVOFF_HEADWISE / KVOFF_CONSENSUS_GROUP); ids ascending, sel_cnt_dev[i]
+ * <= k_stride entries per set.  q_dev [n_req][Hq][d]; mass_dev [n_req][Hq]
+ * fp64.  Enqueued on `stream`.  Errors: EINVAL, ERANGE, ESTATE (unknown
+ * request, layer not offloaded), EHIP. */
+int kvoff_attention_mass(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* req_ids,
+                         int32_t mode, const void* q_dev, const int32_t* sel_idx_dev,
+                         const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
+                         double* mass_dev, void* stream);
 
 /* ------------------------------------------------------------- admission */
 

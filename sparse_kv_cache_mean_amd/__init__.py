@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libkvoff.so")
 KVOFF_OK = 0
 KVOFF_EINVAL, KVOFF_ENOMEM, KVOFF_ENODEV, KVOFF_EHIP, KVOFF_ERANGE, KVOFF_ESTATE = range(-1, -7, -1)
 KVOFF_F16, KVOFF_BF16 = 1, 2
-KVOFF_SOLOHEAD, KVOFF_HEADWISE, KVOFF_CONSENSUS = 0, 1, 2
+KVOFF_SOLOHEAD, KVOFF_HEADWISE, KVOFF_CONSENSUS, KVOFF_CONSENSUS_GROUP = 0, 1, 2, 3
 KVOFF_QK_MFMA, KVOFF_QK_VALU = 0, 1
 KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA, KVOFF_ENGINE_STAGED = 0, 1, 2
 KVOFF_HOST_COHERENT, KVOFF_HOST_NONCOHERENT = 0, 1
@@ -32,7 +32,7 @@ KVOFF_MAX_BATCH = 128
 
 EXPORTS = (
     "kvoff_create", "kvoff_destroy", "kvoff_record_bytes", "kvoff_set_consensus_lambda",
-    "kvoff_set_attention_qk",
+    "kvoff_set_attention_qk", "kvoff_attention_mass",
     "kvoff_register_request",
     "kvoff_host_record", "kvoff_offload_blocks", "kvoff_select", "kvoff_recall",
     "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_read",
@@ -132,6 +132,7 @@ def lib() -> ctypes.CDLL:
     L.kvoff_workspace_size.restype = sz
     L.kvoff_step.argtypes = [_vp, P(kvoff_step_args)]
     L.kvoff_probe_read.argtypes = [_vp, i64, _vp, i32, _vp]
+    L.kvoff_attention_mass.argtypes = [_vp, i32, i32, _vp, i32, _vp, _vp, _vp, i32, f32, _vp, _vp]
     L.kvoff_admission_defaults.argtypes = [P(kvoff_admission_policy)]
     L.kvoff_admission_defaults.restype = None
     L.kvoff_admission_plan.argtypes = [P(kvoff_admission_policy), i32, ctypes.c_double, _vp, P(i32)]
@@ -144,7 +145,7 @@ def lib() -> ctypes.CDLL:
     for name in ("kvoff_create", "kvoff_destroy", "kvoff_register_request", "kvoff_host_record",
                  "kvoff_set_consensus_lambda", "kvoff_set_attention_qk",
                  "kvoff_offload_blocks", "kvoff_select", "kvoff_recall", "kvoff_sparse_decode",
-                 "kvoff_step", "kvoff_probe_read", "kvoff_admission_plan", "kvoff_make_resident",
+                 "kvoff_step", "kvoff_probe_read", "kvoff_attention_mass", "kvoff_admission_plan", "kvoff_make_resident",
                  "kvoff_release_resident"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -320,6 +321,14 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
     if tm is not None:
         res["timing"] = tm.as_dict()
     return res
+
+
+def kvoff_attention_mass(ctx: int, layer: int, req_ids: Sequence[int], mode: int, q, sel_idx,
+                         sel_cnt, k_stride: int, scale: float, mass, stream=None) -> None:
+    ids = _i32_array(req_ids)
+    _check(lib().kvoff_attention_mass(ctx, layer, len(req_ids), ctypes.cast(ids, _vp), mode,
+                                      _ptr(q), _ptr(sel_idx), _ptr(sel_cnt), k_stride, scale,
+                                      _ptr(mass), _stream(stream)))
 
 
 def kvoff_probe_read(ptr, n_bytes: int, sink, n_wg: int = 0, stream=None) -> None:

@@ -259,8 +259,7 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
     return fail(KVOFF_ERANGE, "layer %d outside [0, %d)", layer, ctx->cfg.num_layers);
   if (!q_dev || !digest_dev || !topk || !scores_dev || !sel_idx_dev || !sel_cnt_dev)
     return fail(KVOFF_EINVAL, "NULL buffer argument");
-  if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE && mode != KVOFF_CONSENSUS)
-    return fail(KVOFF_EINVAL, "mode %d", mode);
+  if (layout_of(mode) < 0) return fail(KVOFF_EINVAL, "mode %d", mode);
   if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
   int64_t max_nb = 0;
   for (int i = 0; i < n_req; ++i) {
@@ -278,9 +277,8 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
   hipStream_t s = (hipStream_t)stream;
   st = launch_score(ctx, b, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
   if (st) return st;
-  // a consensus selection is one shared set, laid out like SoloHead's
-  const int32_t sel_mode = mode == KVOFF_HEADWISE ? KVOFF_HEADWISE : KVOFF_SOLOHEAD;
-  return launch_topk(ctx, b, topk, sel_mode, scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
+  // consensus selections use the layout of their scope (shared or per KV head)
+  return launch_topk(ctx, b, topk, layout_of(mode), scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
                      k_stride, s);
 }
 
@@ -331,8 +329,8 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
   if ((st = check_layer_offloaded(ctx, layer, b))) return st;
   if (!sel_idx_dev || !sel_cnt_dev || !slot_pool_dev || !block_table_dev)
     return fail(KVOFF_EINVAL, "NULL buffer argument");
-  if (mode == KVOFF_CONSENSUS) mode = KVOFF_SOLOHEAD;  // one shared set
-  if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE) return fail(KVOFF_EINVAL, "mode %d", mode);
+  mode = layout_of(mode);  // consensus modes use the layout of their scope
+  if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
   if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
   if ((pool_hit_dev == nullptr) != (pool_slot_dev == nullptr))
     return fail(KVOFF_EINVAL, "pool_hit_dev and pool_slot_dev must both be given or both NULL");
@@ -368,8 +366,8 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
   if (n_req == 0) return KVOFF_OK;
   if (!q_dev || !slot_pool_dev || !block_table_dev || !sel_idx_dev || !sel_cnt_dev || !out_dev)
     return fail(KVOFF_EINVAL, "NULL buffer argument");
-  if (mode == KVOFF_CONSENSUS) mode = KVOFF_SOLOHEAD;  // one shared set
-  if (mode != KVOFF_SOLOHEAD && mode != KVOFF_HEADWISE) return fail(KVOFF_EINVAL, "mode %d", mode);
+  mode = layout_of(mode);  // consensus modes use the layout of their scope
+  if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
   if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
   size_t need = attend_ws_bytes(ctx, n_req, k_stride);
   if (need > 0 && (!ws_dev || ws_bytes < need))
@@ -377,6 +375,28 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
   KVOFF_HIP(hipSetDevice(ctx->device));
   return launch_attend(ctx, b, mode, q_dev, slot_pool_dev, block_table_dev, sel_idx_dev,
                        sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
+}
+
+int kvoff_attention_mass(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* req_ids,
+                         int32_t mode, const void* q_dev, const int32_t* sel_idx_dev,
+                         const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
+                         double* mass_dev, void* stream) {
+  if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
+  BatchIds b;
+  int st = make_batch(ctx, n_req, req_ids, &b);
+  if (st) return st;
+  if (n_req == 0) return KVOFF_OK;
+  if (layer < 0 || layer >= ctx->cfg.num_layers)
+    return fail(KVOFF_ERANGE, "layer %d outside [0, %d)", layer, ctx->cfg.num_layers);
+  if (!q_dev || !sel_idx_dev || !sel_cnt_dev || !mass_dev)
+    return fail(KVOFF_EINVAL, "NULL buffer argument");
+  mode = layout_of(mode);
+  if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
+  if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
+  if ((st = check_layer_offloaded(ctx, layer, b))) return st;
+  KVOFF_HIP(hipSetDevice(ctx->device));
+  return launch_mass(ctx, b, layer, mode, q_dev, sel_idx_dev, sel_cnt_dev, k_stride, scale,
+                     mass_dev, (hipStream_t)stream);
 }
 
 int kvoff_probe_read(const void* ptr, int64_t n_bytes, void* dev_sink, int32_t n_wg,

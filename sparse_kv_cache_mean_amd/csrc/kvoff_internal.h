@@ -83,6 +83,18 @@ int fail(int status, const char* fmt, ...);
                            hipGetErrorString(e_), __FILE__, __LINE__);             \
   } while (0)
 
+// selection layout of a mode: one set per KV head (KVOFF_HEADWISE) or one
+// shared set (KVOFF_SOLOHEAD); -1 for an unknown mode
+inline int32_t layout_of(int32_t mode) {
+  switch (mode) {
+    case KVOFF_SOLOHEAD:
+    case KVOFF_CONSENSUS: return KVOFF_SOLOHEAD;
+    case KVOFF_HEADWISE:
+    case KVOFF_CONSENSUS_GROUP: return KVOFF_HEADWISE;
+    default: return -1;
+  }
+}
+
 // check a batch and fill BatchIds; ESTATE for an unknown id
 int make_batch(const kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, BatchIds* out);
 
@@ -125,6 +137,10 @@ int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, kvoff_sta
 int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, kvoff_stats* stats,
                   hipStream_t stream);
 void stage_pool_destroy(kvoff_ctx* ctx);
+
+int launch_mass(const kvoff_ctx* ctx, const BatchIds& b, int32_t layer, int32_t mode,
+                const void* q_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
+                int32_t k_stride, float scale, double* mass_dev, hipStream_t stream);
 
 // split policy of the attention kernel: number of splits per (request, KV head)
 int attend_splits(int32_t k_stride);

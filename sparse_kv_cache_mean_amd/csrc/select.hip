@@ -15,6 +15,11 @@
 // 1 KiB chunk of a block's [Hkv][d] digest row (coalesced dwordx4 loads), does
 // fp64 FMAs against its slice of u, and the wave reduces with lane shuffles.
 //
+// Consensus modes: across KV heads (KVOFF_CONSENSUS) the per-KV-head sums
+// are combined into one shared score; within a GQA group
+// (KVOFF_CONSENSUS_GROUP) each query head's sum is formed from the q rows in
+// LDS and the group's max + lambda * mean is one score per KV head.
+//
 // topk_kernel: one workgroup per request (per (request, KV head) when
 // headwise) runs an MSB-first radix select over order-preserving 64-bit keys
 // of the fp64 scores (8 passes of 8 bits, LDS histogram), then an ordered
@@ -54,7 +59,7 @@ struct ScoreArgs {
   double lambda;  // consensus mode only
 };
 
-enum { MODE_SOLO = 0, MODE_HEADWISE = 1, MODE_CONSENSUS = 2 };
+enum { MODE_SOLO = 0, MODE_HEADWISE = 1, MODE_CONSENSUS = 2, MODE_GROUP = 3 };
 
 template <bool BF16>
 __device__ __forceinline__ double widen_t(uint16_t h) {
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __syncthreads();
 
   // u_g = sum of the group's G query heads, in fp64: thread (g, 8-dim group)
-  for (int t = tid; t < NC * 32; t += 256) {
+  for (int t = tid; t < (MODE == MODE_GROUP ? 0 : NC * 32); t += 256) {
     const int g = t >> 4, dg = t & 15;
     double s[8];
 #pragma unroll
@@ -132,6 +137,50 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     for (int e = 0; e < 8; ++e) u_s[t * 8 + e] = s[e];
   }
   __syncthreads();
+
+  if constexpr (MODE == MODE_GROUP) {
+    // consensus within each GQA group: per query head h of group g,
+    // s_h = <q_h, D[b][g]>; S_g = max_h s_h + lambda * mean_h s_h.  Lane
+    // holds dims idx..idx+3 of KV head idx/128 in chunk c (chunk c covers
+    // heads 2c and 2c+1); dims past the row contribute nothing.
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_s);
+#pragma unroll
+    for (int k = 0; k < SCORE_BPW; ++k) {
+      const int64_t b = bw + k;
+      double mx[NC], sm[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        mx[c] = -INFINITY;
+        sm[c] = 0.0;
+      }
+      for (int i = 0; i < a.G; ++i) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int idx = c * 256 + lane * 4;
+          double acc = 0.0;
+          if (idx < F) {
+            const int g = idx / kHeadDim, j0 = idx % kHeadDim;
+            const uint2 w = *reinterpret_cast<const uint2*>(q16 + (g * a.G + i) * kHeadDim + j0);
+            acc = fma(widen_t<BF16>((uint16_t)(w.x & 0xffffu)), (double)v[k][c].x, acc);
+            acc = fma(widen_t<BF16>((uint16_t)(w.x >> 16)), (double)v[k][c].y, acc);
+            acc = fma(widen_t<BF16>((uint16_t)(w.y & 0xffffu)), (double)v[k][c].z, acc);
+            acc = fma(widen_t<BF16>((uint16_t)(w.y >> 16)), (double)v[k][c].w, acc);
+          }
+#pragma unroll
+          for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+          mx[c] = fmax(mx[c], acc);
+          sm[c] += acc;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int g = (c * 256 + (lane & 32) * 4) / kHeadDim;
+        if ((lane & 31) == 0 && b < rq.nb && g < a.Hkv)
+          a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = mx[c] + a.lambda * (sm[c] / (double)a.G);
+      }
+    }
+    return;
+  }
 
   double u[NC][4];
 #pragma unroll
@@ -372,6 +421,8 @@ void score_launch(const ScoreArgs& a, int64_t max_nb, int mode, hipStream_t s) {
     score_launch_m<NC, MODE_HEADWISE>(a, max_nb, s);
   else if (mode == KVOFF_CONSENSUS)
     score_launch_m<NC, MODE_CONSENSUS>(a, max_nb, s);
+  else if (mode == KVOFF_CONSENSUS_GROUP)
+    score_launch_m<NC, MODE_GROUP>(a, max_nb, s);
   else
     score_launch_m<NC, MODE_SOLO>(a, max_nb, s);
 }

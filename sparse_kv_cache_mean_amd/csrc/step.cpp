@@ -105,7 +105,7 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
       ctx->ev_timing.push_back(e);
     }
   }
-  const int sets = A->mode == KVOFF_HEADWISE ? ctx->cfg.num_kv_heads : 1;
+  const int sets = layout_of(A->mode) == KVOFF_HEADWISE ? ctx->cfg.num_kv_heads : 1;
   const int64_t q_row = (int64_t)ctx->cfg.num_q_heads * ctx->cfg.head_dim;  // elements per request
 
   auto recall_l = [&](int li) -> int {

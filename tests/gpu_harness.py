@@ -147,7 +147,7 @@ class Buffers:
 
 def make_buffers(c: Case, mode: int) -> Buffers:
     s, B = c.s, c.B
-    sets = s.Hkv if mode == kv.KVOFF_HEADWISE else 1
+    sets = s.Hkv if mode in (kv.KVOFF_HEADWISE, kv.KVOFF_CONSENSUS_GROUP) else 1
     scores = torch.empty((B, sets, c.nb_max), dtype=torch.float64, device="cuda")
     sel_idx = torch.empty((B, sets, c.k_stride), dtype=torch.int32, device="cuda")
     sel_cnt = torch.empty((B,), dtype=torch.int32, device="cuda")

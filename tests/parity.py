@@ -38,6 +38,20 @@ def shared_set(sl, mode):
     return sl.sel_c if mode == kv.KVOFF_CONSENSUS else sl.sel
 
 
+def per_head(mode) -> bool:
+    """Modes with one block set per KV head (headwise layout)."""
+    return mode in (kv.KVOFF_HEADWISE, kv.KVOFF_CONSENSUS_GROUP)
+
+
+def head_sets(sl, mode):
+    """[Hkv][K] block sets of a per-KV-head mode."""
+    return sl.sel_gc if mode == kv.KVOFF_CONSENSUS_GROUP else sl.sel_g
+
+
+def block_sets(sl, mode):
+    return list(head_sets(sl, mode)) if per_head(mode) else [shared_set(sl, mode)]
+
+
 def check_selection(c, l, mode, bufs, slices):
     sel = bufs.sel_idx.cpu().numpy()
     cnt = bufs.sel_cnt.cpu().numpy()
@@ -52,10 +66,11 @@ def check_selection(c, l, mode, bufs, slices):
             assert sel[r, 0, :K].tolist() == shared_set(sl, mode).tolist(), (l, r)
             assert np.all(sel[r, 0, K:] == -1)
         else:
+            Sh = sl.Sgc if mode == kv.KVOFF_CONSENSUS_GROUP else sl.Sg
             for g in range(c.s.Hkv):
-                assert np.allclose(sc[r, g, :nb], sl.Sg[g], rtol=0,
-                                   atol=1e-9 * (1 + np.abs(sl.Sg[g]).max()))
-                assert sel[r, g, :K].tolist() == sl.sel_g[g].tolist(), (l, r, g)
+                assert np.allclose(sc[r, g, :nb], Sh[g], rtol=0,
+                                   atol=1e-9 * (1 + np.abs(Sh[g]).max()))
+                assert sel[r, g, :K].tolist() == head_sets(sl, mode)[g].tolist(), (l, r, g)
                 assert np.all(sel[r, g, K:] == -1)
 
 
@@ -64,13 +79,12 @@ def expected_transfers(c, l, mode, slices, with_pool_hits):
     for r in range(c.B):
         sl = slices[(l, r)]
         hit = sl.lr.pool if with_pool_hits else None
-        sets = list(sl.sel_g) if mode == kv.KVOFF_HEADWISE else [shared_set(sl, mode)]
-        for s in sets:
+        for s in block_sets(sl, mode):
             n_sel += len(s)
             miss = [b for b in s.tolist() if not (hit is not None and hit[b])]
             n_items += len(miss)
             n_hits += len(s) - len(miss)
-            if mode != kv.KVOFF_HEADWISE:
+            if not per_head(mode):
                 n_tr += len(oracle.runs(s, hit)[0])
             else:
                 n_tr += oracle.headwise_transfers(s[None, :], [len(s)], hit)
@@ -99,12 +113,11 @@ def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats
         sl = slices[(l, r)]
         K = sl.K
         hit = sl.lr.pool if with_pool_hits else np.zeros(sl.lr.rq.nb, np.uint8)
-        sets = list(sl.sel_g) if mode == kv.KVOFF_HEADWISE else [shared_set(sl, mode)]
-        for g, sset in enumerate(sets):
+        for g, sset in enumerate(block_sets(sl, mode)):
             want = workloads.block_records(sl, sset.tolist())  # [K][Hkv][2][bs][d]
             for i, b in enumerate(sset.tolist()):
                 ent = int(table[r, g, i])
-                hw = mode == kv.KVOFF_HEADWISE
+                hw = per_head(mode)
                 if hit[b]:
                     exp = int(ps[r, b]) * (s.Hkv if hw else 1) + (g if hw else 0)
                 elif compact:
@@ -122,7 +135,7 @@ def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats
             assert np.all(table[r, g, K:] == -1)
     if stats is not None:
         exp = expected_transfers(c, l, mode, slices, with_pool_hits)
-        item = slice_b if mode == kv.KVOFF_HEADWISE else rec
+        item = slice_b if per_head(mode) else rec
         if compact:  # bulk copies of the staging buffer
             exp["transfers"] = -(-exp["items_recalled"] * item // STAGE_CHUNK)
         for k, v in exp.items():
@@ -136,8 +149,8 @@ def oracle_attention(c, l, mode, slices):
     for r in range(c.B):
         sl = slices[(l, r)]
         lr = sl.lr
-        if mode == kv.KVOFF_HEADWISE:
-            out[r] = oracle.attend_headwise_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, sl.sel_g)
+        if per_head(mode):
+            out[r] = oracle.attend_headwise_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, head_sets(sl, mode))
         else:
             out[r] = oracle.attend_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, shared_set(sl, mode))
     return out

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import sparse_kv_cache_mean_amd as kv
 import synth
 from tests import gpu_harness as H
@@ -16,17 +17,18 @@ from tests import workloads
 pytestmark = pytest.mark.gpu
 
 
-def _slices(s, layers, reqs=None, lam=None):
+def _slices(s, layers, reqs=None, lam=None, group_lam=None):
     reqs = reqs or synth.request_draws(s)
     out = {}
     for l in layers:
         for r, rq in enumerate(reqs):
-            out[(l, r)] = workloads.make_slice(s, l, r, rq, lam=lam)
+            out[(l, r)] = workloads.make_slice(s, l, r, rq, lam=lam, group_lam=group_lam)
     return reqs, out
 
 
-def _case(s, layers, with_pool_hits=False, host_kind=kv.KVOFF_HOST_COHERENT, reqs=None, lam=None):
-    reqs, sl = _slices(s, layers, reqs, lam)
+def _case(s, layers, with_pool_hits=False, host_kind=kv.KVOFF_HOST_COHERENT, reqs=None, lam=None,
+          group_lam=None):
+    reqs, sl = _slices(s, layers, reqs, lam, group_lam)
     inputs = {k: v.lr for k, v in sl.items()}
     c = H.build_case(s, inputs, layers, reqs, host_kind=host_kind, with_pool_hits=with_pool_hits)
     return c, sl
@@ -136,17 +138,38 @@ def test_consensus_rule(lam, engine):
         H.destroy(c)
 
 
+@pytest.mark.parametrize("lam", [0.5, 1.0])
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
+def test_group_consensus_rule(lam, engine):
+    """The consensus rule with the GQA-group scope: one set per KV head from
+    max + lambda * mean over the group's query heads, recalled and attended
+    in the headwise layout."""
+    H.log(f"[group consensus] lambda {lam} engine {engine}")
+    c, sl = _case(HW, [0], with_pool_hits=True, group_lam=lam)
+    try:
+        kv.kvoff_set_consensus_lambda(c.ctx, lam)
+        stats, _ = _full_check(c, sl, 0, kv.KVOFF_CONSENSUS_GROUP, engine, with_pool_hits=True)
+        H.log(f"  stats {stats}")
+        diff = sum(len(set(sl[(0, r)].sel_gc[g].tolist()) ^ set(sl[(0, r)].sel_g[g].tolist()))
+                   for r in range(c.B) for g in range(HW.Hkv))
+        H.log(f"  blocks differing from the headwise sets: {diff}")
+    finally:
+        H.destroy(c)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 2), (16, 16), (64, 4)])
 def test_group_sizes(Hq, Hkv):
     H.log(f"[groups] Hq {Hq} Hkv {Hkv}")
     s = synth.spec(2, B=2, Hq=Hq, Hkv=Hkv, ctx=2000, k=12, hot=5, headwise=Hkv > 1)
-    c, sl = _case(s, [0], lam=0.5)  # the context's default lambda
+    c, sl = _case(s, [0], lam=0.5, group_lam=0.5)  # the context's default lambda
     try:
         _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
         if Hkv > 1:
             _full_check(c, sl, 0, kv.KVOFF_HEADWISE, kv.KVOFF_ENGINE_ZEROCOPY)
         # consensus across KV heads (also for a single KV head: (1 + lambda) * S)
         _full_check(c, sl, 0, kv.KVOFF_CONSENSUS, kv.KVOFF_ENGINE_ZEROCOPY)
+        # consensus within each GQA group (a group of one head: (1 + lambda) * S_g)
+        _full_check(c, sl, 0, kv.KVOFF_CONSENSUS_GROUP, kv.KVOFF_ENGINE_ZEROCOPY)
     finally:
         H.destroy(c)
 
@@ -194,6 +217,47 @@ def test_attention_qk_valu_rejects_large_groups():
         assert e.value.status == kv.KVOFF_EINVAL
         with pytest.raises(kv.KvoffError):
             kv.kvoff_set_attention_qk(c.ctx, 7)
+    finally:
+        H.destroy(c)
+
+
+# fp32 logits differ from the oracle's fp64 ones by at most about
+# 128 * 2^-24 * sum_j |q_j K_j| / sqrt(d) (~5e-5 at unit-variance inputs);
+# the kept share moves by at most about twice that.
+MASS_ATOL = 1e-4
+
+
+@pytest.mark.parametrize("which", ["tiny", "hw", "ragged"])
+def test_attention_mass_matches_oracle(which):
+    """kvoff_attention_mass against the oracle for shared and per-KV-head
+    sets, including partial last blocks."""
+    s = {"tiny": TINY, "hw": HW, "ragged": RAGGED}[which]
+    H.log(f"[mass] {which}")
+    lam = 0.5
+    c, sl = _case(s, [0], lam=lam, group_lam=lam)
+    try:
+        modes = [kv.KVOFF_SOLOHEAD, kv.KVOFF_CONSENSUS, kv.KVOFF_CONSENSUS_GROUP] + \
+            ([kv.KVOFF_HEADWISE] if s.headwise else [])
+        for mode in modes:
+            bufs = H.make_buffers(c, mode)
+            kv.kvoff_select(c.ctx, 0, c.rids, c.q[0], c.digest[0], c.nb_max,
+                            [rq.k for rq in c.reqs], mode, bufs.scores, bufs.sel_idx,
+                            bufs.sel_cnt, c.k_stride)
+            mass = torch.full((c.B, s.Hq), float("nan"), dtype=torch.float64, device="cuda")
+            kv.kvoff_attention_mass(c.ctx, 0, c.rids, mode, c.q[0], bufs.sel_idx, bufs.sel_cnt,
+                                    c.k_stride, 1.0 / math.sqrt(s.d), mass)
+            torch.cuda.synchronize()
+            got = mass.cpu().numpy()
+            worst = 0.0
+            for r in range(c.B):
+                x = sl[(0, r)]
+                sets = P.block_sets(x, mode)
+                ref = oracle.attention_mass(x.lr.q, x.lr.K, s.dtype, s.bs,
+                                            np.stack(sets) if len(sets) > 1 else sets[0])
+                err = np.abs(got[r] - ref).max()
+                worst = max(worst, err)
+                assert err <= MASS_ATOL, (mode, r, err)
+            H.log(f"  mode {mode}: mean mass {got.mean():.4f}, max |err| {worst:.2e}")
     finally:
         H.destroy(c)
 

@@ -37,6 +37,8 @@ class Slice:
     Sc: Optional[np.ndarray] = None    # [nb] consensus scores (when lam is given)
     sel_c: Optional[np.ndarray] = None  # [K] consensus selection
     lam: Optional[float] = None
+    Sgc: Optional[np.ndarray] = None    # [Hkv][nb] GQA-group consensus scores (group_lam)
+    sel_gc: Optional[np.ndarray] = None  # [Hkv][K] GQA-group consensus selections
 
     @property
     def K(self) -> int:
@@ -54,8 +56,9 @@ def boundary(S: np.ndarray, K: int):
 
 def condition(s: synth.Spec, lr: synth.LayerRequest, min_gap: float = MIN_GAP,
               headwise: Optional[bool] = None, enforce: bool = True,
-              lam: Optional[float] = None) -> Slice:
-    """lam: also condition and select the consensus ranking with that lambda."""
+              lam: Optional[float] = None, group_lam: Optional[float] = None) -> Slice:
+    """lam: also condition and select the consensus ranking with that lambda;
+    group_lam: also the per-KV-head GQA-group consensus rankings."""
     headwise = s.headwise if headwise is None else headwise
     rq = lr.rq
     K = min(rq.k, rq.nb)
@@ -65,8 +68,11 @@ def condition(s: synth.Spec, lr: synth.LayerRequest, min_gap: float = MIN_GAP,
         S = oracle.score(lr.q, s.dtype, D)
         Sg = oracle.score_headwise(lr.q, s.dtype, D) if headwise else None
         Sc = oracle.score_consensus(lr.q, s.dtype, D, lam) if lam is not None else None
+        Sgc = (oracle.score_group_consensus(lr.q, s.dtype, D, group_lam)
+               if group_lam is not None else None)
         rankings = [S] + ([Sg[g] for g in range(s.Hkv)] if headwise else []) + \
-            ([Sc] if Sc is not None else [])
+            ([Sc] if Sc is not None else []) + \
+            ([Sgc[g] for g in range(s.Hkv)] if Sgc is not None else [])
         worst, bad = float("inf"), None
         for R in rankings:
             gap, b = boundary(R, K)
@@ -87,15 +93,18 @@ def condition(s: synth.Spec, lr: synth.LayerRequest, min_gap: float = MIN_GAP,
     sel = oracle.select(S, rq.k)
     sel_g = np.stack([oracle.select(Sg[g], rq.k) for g in range(s.Hkv)]) if headwise else None
     sel_c = oracle.select(Sc, rq.k) if Sc is not None else None
-    return Slice(s, lr, D, S, Sg, sel, sel_g, worst, redraws, Sc, sel_c, lam)
+    sel_gc = (np.stack([oracle.select(Sgc[g], rq.k) for g in range(s.Hkv)])
+              if Sgc is not None else None)
+    return Slice(s, lr, D, S, Sg, sel, sel_g, worst, redraws, Sc, sel_c, lam, Sgc, sel_gc)
 
 
 def make_slice(s: synth.Spec, layer: int, req: int, rq: Optional[synth.Request] = None,
-               enforce: bool = True, lam: Optional[float] = None) -> Slice:
+               enforce: bool = True, lam: Optional[float] = None,
+               group_lam: Optional[float] = None) -> Slice:
     if rq is None:
         rq = synth.request_draws(s)[req]
     lr = synth.gen_layer_request(s, layer, req, rq)
-    return condition(s, lr, enforce=enforce, lam=lam)
+    return condition(s, lr, enforce=enforce, lam=lam, group_lam=group_lam)
 
 
 def block_records(sl: Slice, blocks) -> np.ndarray:
