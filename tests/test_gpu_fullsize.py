@@ -24,11 +24,11 @@ from tests import workloads
 pytestmark = pytest.mark.gpu
 
 
-def _conditioned(s, layers, reqs):
+def _conditioned(s, layers, reqs, lam=None, group_lam=None):
     sl = {}
     for l in layers:
         for r, rq in enumerate(reqs):
-            sl[(l, r)] = workloads.make_slice(s, l, r, rq)
+            sl[(l, r)] = workloads.make_slice(s, l, r, rq, lam=lam, group_lam=group_lam)
     return sl
 
 
@@ -45,7 +45,7 @@ def _sampled_attention(c, l, mode, bufs, slices, groups):
         Kg = np.ascontiguousarray(lr.K[:, g:g + 1, :])
         Vg = np.ascontiguousarray(lr.V[:, g:g + 1, :])
         qg = lr.q[g * G:(g + 1) * G]
-        sel = sl.sel if mode == kv.KVOFF_SOLOHEAD else sl.sel_g[g]
+        sel = P.head_sets(sl, mode)[g] if P.per_head(mode) else P.shared_set(sl, mode)
         ref = oracle.attend_f32(qg, Kg, Vg, s.dtype, s.bs, sel)
         err = P.check_attention_close(got[r, g * G:(g + 1) * G], ref, f"(layer {l} req {r} group {g})")
         worst = (max(worst[0], err[0]), max(worst[1], err[1]))
@@ -78,6 +78,13 @@ def test_llama3_8b_layer_full_size():
         st2 = H.run_layer(c, 0, kv.KVOFF_SOLOHEAD, bufs, engine=kv.KVOFF_ENGINE_DMA, want_stats=True)
         torch.cuda.synchronize()
         P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st2)
+        P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
+        H.log("  staged recall")
+        c.pool.zero_()
+        st3 = H.run_layer(c, 0, kv.KVOFF_SOLOHEAD, bufs, engine=kv.KVOFF_ENGINE_STAGED,
+                          want_stats=True)
+        torch.cuda.synchronize()
+        P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st3, engine=kv.KVOFF_ENGINE_STAGED)
         P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
     finally:
         H.destroy(c)
@@ -113,8 +120,9 @@ def test_headwise_vs_solohead_full_size():
     t0 = time.time()
     s = synth.spec(5)  # llama3-8b shapes, per-KV-head top-64 vs shared, 25% pool hits
     reqs = synth.request_draws(s)
-    H.log("[full headwise-vs-solohead] conditioning (SoloHead + 8 per-head rankings)")
-    sl = _conditioned(s, [0], reqs)
+    H.log("[full headwise-vs-solohead] conditioning (SoloHead, 8 per-head, consensus and "
+          "8 per-group consensus rankings)")
+    sl = _conditioned(s, [0], reqs, lam=0.5, group_lam=0.5)
     H.log(f"  built in {time.time() - t0:.1f} s; offloading")
     c = H.build_case(s, {k: v.lr for k, v in sl.items()}, [0], reqs, with_pool_hits=True,
                      two_regions=False)
@@ -132,6 +140,26 @@ def test_headwise_vs_solohead_full_size():
                 report[(mode, engine)] = st
                 H.log(f"  mode {mode} engine {engine}: {st}, mean transfer "
                       f"{st['bytes'] / max(1, st['transfers']) / 1024:.1f} KiB")
+        for mode in (kv.KVOFF_CONSENSUS, kv.KVOFF_CONSENSUS_GROUP):  # lambda 0.5 (default)
+            bufs = H.make_buffers(c, mode)
+            st = H.run_layer(c, 0, mode, bufs, with_pool_hits=True, want_stats=True)
+            torch.cuda.synchronize()
+            P.check_selection(c, 0, mode, bufs, sl)
+            P.check_recall(c, 0, mode, bufs, sl, with_pool_hits=True, stats=st)
+            _sampled_attention(c, 0, mode, bufs, sl, [(5 * r + 1) % s.Hkv for r in range(c.B)])
+            # attention mass of two sampled requests against the oracle
+            mass = torch.empty((c.B, s.Hq), dtype=torch.float64, device="cuda")
+            kv.kvoff_attention_mass(c.ctx, 0, c.rids, mode, c.q[0], bufs.sel_idx, bufs.sel_cnt,
+                                    c.k_stride, 1.0 / math.sqrt(s.d), mass)
+            torch.cuda.synchronize()
+            got = mass.cpu().numpy()
+            for r in (0, c.B - 1):
+                x = sl[(0, r)]
+                sets = P.block_sets(x, mode)
+                ref = oracle.attention_mass(x.lr.q, x.lr.K, s.dtype, s.bs,
+                                            np.stack(sets) if len(sets) > 1 else sets[0])
+                assert np.abs(got[r] - ref).max() <= 1e-4, (mode, r)
+            H.log(f"  mode {mode}: {st}; mean mass {got.mean():.4f}")
         solo, hw = report[(0, 0)], report[(1, 0)]
         assert hw["transfers"] > 4 * solo["transfers"]  # per-head recall fragments
         unions = [oracle.union_count(sl[(0, r)].sel_g, [sl[(0, r)].K] * s.Hkv) for r in range(c.B)]
