@@ -139,7 +139,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   const int quad = lane >> 4, col = lane & 15;
 
   const ReqDev rq = a.reqs[a.batch.id[r]];
-  const int cnt = a.sel_cnt[r];
+  const int cnt = min(a.sel_cnt[r], a.k_stride);
+  // a split past the request's selection has nothing to do: it writes no
+  // partial, and the combine reads only the splits that hold blocks
+  if (s * ATT_WAVES * a.bpw >= cnt) return;  // uniform over the workgroup
   const int64_t row = a.hw ? ((int64_t)r * a.Hkv + g) * a.k_stride : (int64_t)r * a.k_stride;
   const int i0 = (s * ATT_WAVES + wave) * a.bpw;
   const int i1 = min(i0 + a.bpw, cnt);
@@ -359,26 +362,30 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 
 }
 
-// blocks per wave (at most 4: the per-wave index cache)
 // One workgroup per (request, head), one thread per dim: single-pass merge
-// of the splits in order, loads batched 8 splits at a time.
-__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, float* out, int S) {
+// of the request's non-empty splits in order (ceil(count / blocks per
+// split) of the S), loads batched 8 splits at a time.
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, float* out, int S,
+                                                          const int32_t* sel_cnt, int k_stride,
+                                                          int per_split, int Hq) {
   const int64_t rh = blockIdx.x;  // request * Hq + head
   const int j = threadIdx.x;
   const float* P = part + rh * S * PART;
+  const int cnt = min(sel_cnt[rh / Hq], k_stride);
+  const int Sr = min(S, (cnt + per_split - 1) / per_split);
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 8) {
+  for (int s0 = 0; s0 < Sr; s0 += 8) {
     float m[8], l[8], o[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int t = min(s0 + k, S - 1);
+      const int t = min(s0 + k, Sr - 1);
       m[k] = P[t * PART];
       l[k] = P[t * PART + 1];
       o[k] = P[t * PART + 2 + j];
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      if (s0 + k >= S || m[k] == -INFINITY) continue;
+      if (s0 + k >= Sr || m[k] == -INFINITY) continue;
       if (m[k] > M) {
         const float f = M == -INFINITY ? 0.f : exp2f(M - m[k]);
         L = fmaf(L, f, l[k]);
@@ -475,7 +482,7 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   }
   KVOFF_HIP(hipGetLastError());
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
-                     a.part, out, a.S);
+                     a.part, out, a.S, sel_cnt, k_stride, ATT_WAVES * a.bpw, a.Hq);
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }
