@@ -387,8 +387,10 @@ int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, do
  * from the pinned store into HBM slots [first_slot, first_slot + nb) of
  * slot_pool_dev, then sets pool_hit_dev[b] = 1 and pool_slot_dev[b] =
  * first_slot + b for b < nb (the request's row of the maps kvoff_recall
- * takes).  Errors: EINVAL, ERANGE (slots past n_slots), ESTATE (layer not
- * offloaded), EHIP. */
+ * takes).  Enqueued on `stream`: the caller orders later recalls after it
+ * (same stream or an event) and keeps the slots out of every recall region.
+ * Errors: EINVAL, ERANGE (slots past n_slots), ESTATE (layer not offloaded),
+ * EHIP. */
 int kvoff_make_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, void* slot_pool_dev,
                         int64_t n_slots, int64_t first_slot, uint8_t* pool_hit_dev,
                         int32_t* pool_slot_dev, void* stream);

@@ -1,0 +1,205 @@
+/*
+ * abi_roundtrip.c - drives libkvoff.so through its C ABI alone (no Python)
+ * and checks every stage against the plain C oracle.  Test infrastructure.
+ *
+ * One request, one layer: Hq = 8, Hkv = 2, d = 128, blocks of 16 tokens, a
+ * ragged context of 1000 tokens (63 blocks, the last holding 8 tokens),
+ * top-20, both storage types.  Inputs come from the seeded generator.
+ *   digests           bit-exact against oracle_digest
+ *   selection         equal to oracle_select of the oracle's fp64 scores
+ *                     (the test first checks that rank 20 and rank 21 are
+ *                     at least 1e-3 apart, so the decision is unambiguous)
+ *   recalled records  byte-equal to oracle_records of the selected blocks
+ *   transfers         equal to oracle_runs
+ *   attention         within 2e-3 of oracle_attend_f32
+ * Exit status 0 and a final "PASS" line on success.
+ */
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "kvoff.h"
+#include "kvoff_oracle.h"
+#include "synth.h"
+
+#define HQ 8
+#define HKV 2
+#define D 128
+#define BS 16
+#define CTX 1000
+#define NB ((CTX + BS - 1) / BS)
+#define TOPK 20
+
+static int failures = 0;
+
+#define CHECK(cond, ...)                  \
+  do {                                    \
+    if (!(cond)) {                        \
+      fprintf(stderr, "FAIL: " __VA_ARGS__); \
+      fprintf(stderr, "\n");              \
+      ++failures;                         \
+    }                                     \
+  } while (0)
+
+#define HIPOK(call)                                                                  \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess) {                                                          \
+      fprintf(stderr, "%s: %s\n", #call, hipGetErrorString(e_));                     \
+      exit(2);                                                                       \
+    }                                                                                \
+  } while (0)
+
+#define KVOK(call)                                                                   \
+  do {                                                                               \
+    int s_ = (call);                                                                 \
+    if (s_ != KVOFF_OK) {                                                            \
+      fprintf(stderr, "%s: %s (%s)\n", #call, kvoff_strerror(s_), kvoff_last_error()); \
+      exit(2);                                                                       \
+    }                                                                                \
+  } while (0)
+
+static int by_desc(const void* a, const void* b) {
+  double x = *(const double*)a, y = *(const double*)b;
+  return (x < y) - (x > y);
+}
+
+static void run(int dtype) {
+  const int sdt = dtype == KVOFF_BF16 ? SYNTH_BF16 : SYNTH_F16;
+  const int odt = sdt; /* the oracle uses the same codes: 1 fp16, 2 bf16 */
+  const uint64_t seed = 4242 + (uint64_t)dtype;
+  const size_t n_kv = (size_t)CTX * HKV * D;
+  uint16_t* q = malloc(sizeof(uint16_t) * HQ * D);
+  uint16_t* K = malloc(sizeof(uint16_t) * n_kv);
+  uint16_t* V = malloc(sizeof(uint16_t) * n_kv);
+  synth_q(seed, 0, 0, HQ, D, sdt, q);
+  synth_kv(seed, SYNTH_TAG_K, 0, 0, CTX, HKV, D, BS, NULL, NULL, NULL, 0.0, sdt, K);
+  synth_kv(seed, SYNTH_TAG_V, 0, 0, CTX, HKV, D, BS, NULL, NULL, NULL, 0.0, sdt, V);
+
+  /* oracle */
+  float* D_ref = malloc(sizeof(float) * NB * HKV * D);
+  double S_ref[NB], S_sorted[NB];
+  int32_t sel_ref[TOPK];
+  oracle_digest(K, odt, CTX, HKV, D, BS, D_ref);
+  oracle_score(q, odt, HQ, HKV, D, D_ref, NB, S_ref);
+  memcpy(S_sorted, S_ref, sizeof S_ref);
+  qsort(S_sorted, NB, sizeof(double), by_desc);
+  const double gap = S_sorted[TOPK - 1] - S_sorted[TOPK];
+  CHECK(gap >= 1e-3, "dtype %d: boundary gap %g below 1e-3 (choose another seed)", dtype, gap);
+  const int64_t k_ref = oracle_select(S_ref, NB, TOPK, sel_ref);
+  CHECK(k_ref == TOPK, "oracle selected %lld", (long long)k_ref);
+  float out_ref[HQ * D];
+  oracle_attend_f32(q, K, V, odt, CTX, HQ, HKV, D, BS, sel_ref, TOPK, out_ref);
+  uint16_t* rec_ref = malloc(sizeof(uint16_t) * (size_t)NB * HKV * 2 * BS * D);
+  oracle_records(K, V, CTX, HKV, D, BS, rec_ref);
+  const int64_t runs_ref = oracle_runs(sel_ref, TOPK, NULL, NULL, NULL);
+
+  /* library */
+  kvoff_config cfg = {1, HQ, HKV, D, BS, dtype, 4, KVOFF_HOST_COHERENT, NB};
+  kvoff_ctx* ctx = NULL;
+  KVOK(kvoff_create(&cfg, &ctx));
+  int32_t rid = -1;
+  KVOK(kvoff_register_request(ctx, CTX, &rid));
+  const int64_t rec_bytes = kvoff_record_bytes(ctx);
+  CHECK(rec_bytes == oracle_rec_bytes(HKV, BS, D, 2), "record bytes %lld", (long long)rec_bytes);
+
+  void *dK, *dV, *dq, *pool, *ws;
+  float *dD, *dout;
+  double* dS;
+  int32_t *dsel, *dcnt, *dtab;
+  const int n_slots = TOPK;
+  HIPOK(hipMalloc(&dK, n_kv * 2));
+  HIPOK(hipMalloc(&dV, n_kv * 2));
+  HIPOK(hipMalloc(&dq, HQ * D * 2));
+  HIPOK(hipMalloc((void**)&dD, sizeof(float) * NB * HKV * D));
+  HIPOK(hipMalloc((void**)&dS, sizeof(double) * NB));
+  HIPOK(hipMalloc((void**)&dsel, sizeof(int32_t) * TOPK));
+  HIPOK(hipMalloc((void**)&dcnt, sizeof(int32_t)));
+  HIPOK(hipMalloc((void**)&dtab, sizeof(int32_t) * TOPK));
+  HIPOK(hipMalloc(&pool, (size_t)n_slots * rec_bytes));
+  HIPOK(hipMalloc((void**)&dout, sizeof(float) * HQ * D));
+  const size_t ws_bytes = kvoff_workspace_size(ctx, KVOFF_CALL_SPARSE_DECODE, 1, TOPK, KVOFF_SOLOHEAD);
+  HIPOK(hipMalloc(&ws, ws_bytes > 0 ? ws_bytes : 1));
+  HIPOK(hipMemcpy(dK, K, n_kv * 2, hipMemcpyHostToDevice));
+  HIPOK(hipMemcpy(dV, V, n_kv * 2, hipMemcpyHostToDevice));
+  HIPOK(hipMemcpy(dq, q, HQ * D * 2, hipMemcpyHostToDevice));
+
+  const int32_t ids[1] = {rid}, topk[1] = {TOPK};
+  kvoff_stats st;
+  KVOK(kvoff_offload_blocks(ctx, 0, rid, dK, dV, dD, NULL));
+  KVOK(kvoff_select(ctx, 0, 1, ids, dq, dD, NB, topk, KVOFF_SOLOHEAD, dS, dsel, dcnt, TOPK, NULL));
+  KVOK(kvoff_recall(ctx, 0, 1, ids, KVOFF_SOLOHEAD, dsel, dcnt, TOPK, NULL, NULL, 0, pool, n_slots,
+                    0, dtab, KVOFF_ENGINE_ZEROCOPY, &st, NULL));
+  KVOK(kvoff_sparse_decode(ctx, 1, ids, KVOFF_SOLOHEAD, dq, pool, dtab, dsel, dcnt, TOPK,
+                           (float)(1.0 / sqrt((double)D)), dout, ws, ws_bytes, NULL));
+  HIPOK(hipDeviceSynchronize());
+
+  float* D_got = malloc(sizeof(float) * NB * HKV * D);
+  int32_t sel_got[TOPK], cnt_got = 0, tab_got[TOPK];
+  float out_got[HQ * D];
+  uint8_t* pool_got = malloc((size_t)n_slots * rec_bytes);
+  HIPOK(hipMemcpy(D_got, dD, sizeof(float) * NB * HKV * D, hipMemcpyDeviceToHost));
+  HIPOK(hipMemcpy(sel_got, dsel, sizeof sel_got, hipMemcpyDeviceToHost));
+  HIPOK(hipMemcpy(&cnt_got, dcnt, sizeof cnt_got, hipMemcpyDeviceToHost));
+  HIPOK(hipMemcpy(tab_got, dtab, sizeof tab_got, hipMemcpyDeviceToHost));
+  HIPOK(hipMemcpy(out_got, dout, sizeof out_got, hipMemcpyDeviceToHost));
+  HIPOK(hipMemcpy(pool_got, pool, (size_t)n_slots * rec_bytes, hipMemcpyDeviceToHost));
+
+  CHECK(memcmp(D_got, D_ref, sizeof(float) * NB * HKV * D) == 0, "dtype %d: digests differ", dtype);
+  CHECK(cnt_got == TOPK, "dtype %d: count %d", dtype, cnt_got);
+  CHECK(memcmp(sel_got, sel_ref, sizeof sel_ref) == 0, "dtype %d: selection differs", dtype);
+  for (int i = 0; i < TOPK; ++i) {
+    CHECK(tab_got[i] == i, "dtype %d: table[%d] = %d", dtype, i, tab_got[i]);
+    const uint8_t* want = (const uint8_t*)(rec_ref + (size_t)sel_ref[i] * HKV * 2 * BS * D);
+    CHECK(memcmp(pool_got + (size_t)i * rec_bytes, want, (size_t)rec_bytes) == 0,
+          "dtype %d: recalled record of block %d differs", dtype, sel_ref[i]);
+  }
+  CHECK(st.selected == TOPK && st.items_recalled == TOPK && st.pool_hits == 0,
+        "dtype %d: stats selected %lld recalled %lld", dtype, (long long)st.selected,
+        (long long)st.items_recalled);
+  CHECK(st.transfers == runs_ref, "dtype %d: transfers %lld, oracle runs %lld", dtype,
+        (long long)st.transfers, (long long)runs_ref);
+  CHECK(st.bytes == TOPK * rec_bytes, "dtype %d: bytes %lld", dtype, (long long)st.bytes);
+  double worst = 0.0;
+  for (int i = 0; i < HQ * D; ++i) {
+    const double e = fabs((double)out_got[i] - (double)out_ref[i]);
+    if (!(e <= worst)) worst = e; /* NaN propagates */
+  }
+  CHECK(worst <= 2e-3, "dtype %d: attention max abs error %g", dtype, worst);
+  printf("dtype %d: gap %.3g, %lld transfers, attention max abs error %.3g\n", dtype, gap,
+         (long long)st.transfers, worst);
+
+  HIPOK(hipFree(dK));
+  HIPOK(hipFree(dV));
+  HIPOK(hipFree(dq));
+  HIPOK(hipFree(dD));
+  HIPOK(hipFree(dS));
+  HIPOK(hipFree(dsel));
+  HIPOK(hipFree(dcnt));
+  HIPOK(hipFree(dtab));
+  HIPOK(hipFree(pool));
+  HIPOK(hipFree(dout));
+  HIPOK(hipFree(ws));
+  KVOK(kvoff_destroy(ctx));
+  free(q);
+  free(K);
+  free(V);
+  free(D_ref);
+  free(rec_ref);
+  free(D_got);
+  free(pool_got);
+}
+
+int main(void) {
+  run(KVOFF_F16);
+  run(KVOFF_BF16);
+  if (failures) {
+    fprintf(stderr, "%d check(s) failed\n", failures);
+    return 1;
+  }
+  printf("PASS\n");
+  return 0;
+}

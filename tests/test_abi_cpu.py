@@ -70,3 +70,10 @@ def test_null_context_is_rejected():
     assert kv.lib().kvoff_register_request(None, 10, None) == kv.KVOFF_EINVAL
     assert kv.lib().kvoff_step(None, None) == kv.KVOFF_EINVAL
     assert kv.kvoff_workspace_size(None, kv.KVOFF_CALL_SPARSE_DECODE, 1, 1, 0) == 0
+
+
+def test_c_program_compiles_and_links_against_the_abi(tmp_path):
+    """include/kvoff.h is valid C and a C program links libkvoff.so alone."""
+    from tests import cabi
+    exe = cabi.build(str(tmp_path))
+    assert os.path.exists(exe)
