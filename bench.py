@@ -77,12 +77,13 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-overlap", action="store_true",
                    help="skip the overlapped kvoff_step measurement (for clean kernel traces)")
-    p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass"], default=None,
+    p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass", "decode32"], default=None,
                    help="instead of the bench line: fragmentation = recall of the "
                         "headwise-vs-SoloHead workload with every engine; admission = the "
                         "multi-layer step before and after one admission decision; groups = "
                         "interruptible per-request scheduling on the variable-recall layer; "
-                        "mass = attention mass kept and recall volume of every selection mode")
+                        "mass = attention mass kept and recall volume of every selection mode; "
+                        "decode32 = the overlapped 32-layer decode step")
     return p.parse_args()
 
 
@@ -430,6 +431,77 @@ def mass_report(args):
     print(json.dumps(res), flush=True)
 
 
+def decode32_report(args):
+    """The 32-layer decode step (batch 8, context 32768, top-64 per layer,
+    about 34 GB of pinned host KV): kvoff_step over all layers with recall of
+    layer l+1 on a copy stream under select/attention of layer l, against the
+    same step on one stream.  Warm: each figure is the mean of several steps
+    after one untimed step."""
+    sp = synth.spec(3)
+    reqs = synth.request_draws(sp)
+    B, L = len(reqs), sp.L
+    layers = list(range(L))
+    t0 = time.time()
+    log(f"generating and offloading {L} layers x {B} requests")
+    case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                        layers, reqs, keep=lambda l, r: False)
+    log(f"offloaded in {time.time() - t0:.1f} s")
+    mode = kv.KVOFF_SOLOHEAD
+    sets = [H.make_buffers(case, mode) for _ in range(2)]
+    outs = [torch.empty_like(sets[0].out) for _ in layers]
+    compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    topk = [rq.k for rq in reqs]
+
+    def step(copy_stream, want_stats=False, timing=False, grp=0):
+        return kv.kvoff_step(
+            case.ctx, layer_begin=0, layer_end=L, req_ids=case.rids, topk=topk, mode=mode,
+            engine=kv.KVOFF_ENGINE_ZEROCOPY, k_stride=case.k_stride,
+            q=[case.q[l] for l in layers], digest=[case.digest[l] for l in layers],
+            digest_stride=case.nb_max, slot_pool=case.pool, n_slots=case.n_slots,
+            recall_base_slot=case.recall_base, scores=[b.scores for b in sets],
+            sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
+            block_table=[b.table for b in sets], scale=1.0 / math.sqrt(sp.d), out=outs,
+            ws=sets[0].ws, compute_stream=compute, copy_stream=copy_stream,
+            want_stats=want_stats, want_timing=timing, group_requests=grp)
+
+    def timed(copy_stream, n=5, grp=0):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        first = time.perf_counter()
+        step(copy_stream, grp=grp)
+        torch.cuda.synchronize()
+        cold_ms = (time.perf_counter() - first) * 1e3
+        e0.record(compute)
+        for _ in range(n):
+            step(copy_stream, grp=grp)
+        e1.record(compute)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n, cold_ms
+
+    st = step(copy, want_stats=True)
+    over_ms, cold_ms = timed(copy)
+    serial_ms, _ = timed(compute)
+    grp_ms, _ = timed(copy, grp=1)
+    tm = step(copy, timing=True, grp=1)["timing"]
+    copy_peak, _ = link_peaks(case)
+    ideal_ms = st["bytes"] / (copy_peak * 1e9) * 1e3
+    res = {"workload": f"{sp.name}: batch {B}, {L} layers, {sp.Hq}/{sp.Hkv} heads, context "
+                       f"{reqs[0].ctx}, block {sp.bs}, top-{reqs[0].k} per layer, zero-copy recall",
+           "recalled_bytes_per_step": st["bytes"],
+           "overlapped": {"ms_per_step": round(over_ms, 3),
+                          "layer_steps_per_s": round(L * 1e3 / over_ms, 1)},
+           "serial_one_stream": {"ms_per_step": round(serial_ms, 3),
+                                 "layer_steps_per_s": round(L * 1e3 / serial_ms, 1)},
+           "overlapped_request_groups_of_1": {
+               "ms_per_step": round(grp_ms, 3), "layer_steps_per_s": round(L * 1e3 / grp_ms, 1),
+               "mean_request_done_ms": round(tm["mean_request_done_ms"], 3)},
+           "first_step_cold_ms": round(cold_ms, 2),
+           "link_bound": {"pinned_memcpy_gbps": round(copy_peak, 2), "ms_per_step": round(ideal_ms, 3),
+                          "layer_steps_per_s": round(L * 1e3 / ideal_ms, 1)},
+           "overlapped_frac_of_link_bound": round(ideal_ms / over_ms, 4)}
+    H.destroy(case)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -447,6 +519,8 @@ def main():
         return groups_report(args)
     if args.report == "mass":
         return mass_report(args)
+    if args.report == "decode32":
+        return decode32_report(args)
     sp = synth.spec(args.config, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)
