@@ -320,6 +320,13 @@ typedef struct kvoff_step_args {
   /* nullable host pointer: when set, the step records timing events on the
      compute stream and, after synchronising it, fills *timing */
   struct kvoff_step_timing* timing;
+  /* Recalls of odd layers run on a second copy stream, so the recall of
+     layer l+1 is not queued behind the end of layer l's on one stream (each
+     still waits, through events, for its selection and for the attention
+     that last read its buffer set).  NULL: a stream the context creates on
+     first use (non-blocking, default priority).  Unused when copy_stream ==
+     compute_stream (the serial order). */
+  void* copy_stream2;
 } kvoff_step_args;
 
 /* Where the compute stream's time went in one kvoff_step, from HIP timing

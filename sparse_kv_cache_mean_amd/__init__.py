@@ -88,7 +88,7 @@ class kvoff_step_args(ctypes.Structure):
         ("scale", ctypes.c_float), ("out_dev", _vp),
         ("ws_dev", _vp), ("ws_bytes", ctypes.c_size_t),
         ("compute_stream", _vp), ("copy_stream", _vp), ("stats", _vp),
-        ("group_requests", ctypes.c_int32), ("timing", _vp),
+        ("group_requests", ctypes.c_int32), ("timing", _vp), ("copy_stream2", _vp),
     ]
 
 
@@ -274,7 +274,7 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
                pool_hit: Optional[Sequence] = None, pool_slot: Optional[Sequence] = None,
                pool_stride: int = 0, compute_stream=None, copy_stream=None,
                want_stats: bool = False, group_requests: int = 0,
-               want_timing: bool = False) -> Optional[dict]:
+               want_timing: bool = False, copy_stream2=None) -> Optional[dict]:
     """Returns None, or the summed kvoff_stats fields (want_stats) and/or
     the compute-stream timing under "timing" (want_timing)."""
     n_layers = layer_end - layer_begin
@@ -309,6 +309,7 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
     cs = _stream(compute_stream)
     a.compute_stream = cs
     a.copy_stream = _stream(copy_stream) if copy_stream is not None else cs
+    a.copy_stream2 = _stream(copy_stream2) if copy_stream2 is not None else None
     st = kvoff_stats() if want_stats else None
     a.stats = ctypes.cast(ctypes.pointer(st), _vp) if st is not None else None
     a.group_requests = group_requests

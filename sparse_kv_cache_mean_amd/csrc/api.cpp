@@ -157,6 +157,7 @@ int kvoff_destroy(kvoff_ctx* ctx) {
   stage_pool_destroy(ctx);
   for (hipEvent_t e : ctx->ev_group) (void)hipEventDestroy(e);
   for (hipEvent_t e : ctx->ev_timing) (void)hipEventDestroy(e);
+  if (ctx->copy2) (void)hipStreamDestroy(ctx->copy2);
   if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
   if (ctx->stage_buf) (void)hipHostFree(ctx->stage_buf);
   if (ctx->table_host) (void)hipHostFree(ctx->table_host);

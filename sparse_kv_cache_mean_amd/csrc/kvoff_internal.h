@@ -66,6 +66,7 @@ struct kvoff_ctx {
   hipEvent_t ev_stage = nullptr;            // behind the last staged copy
   std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
+  hipStream_t copy2 = nullptr;              // kvoff_step's own second copy stream (lazy)
   bool ev_stage_pending = false;
 };
 

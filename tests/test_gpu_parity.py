@@ -61,11 +61,12 @@ def test_tiny_config_full_parity(engine):
         H.destroy(c)
 
 
-def test_tiny_config_noncoherent_store():
-    H.log("[tiny] noncoherent host store")
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
+def test_tiny_config_noncoherent_store(engine):
+    H.log(f"[tiny] noncoherent host store, engine {engine}")
     c, sl = _case(TINY, [0], host_kind=kv.KVOFF_HOST_NONCOHERENT)
     try:
-        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, engine)
     finally:
         H.destroy(c)
 
@@ -295,7 +296,7 @@ def test_step_overlap_matches_serial_and_oracle(engine):
         compute = torch.cuda.Stream()
         copy = torch.cuda.Stream()
 
-        def step(copy_stream, want_stats=False):
+        def step(copy_stream, want_stats=False, copy2=None):
             return kv.kvoff_step(
                 c.ctx, layer_begin=0, layer_end=len(layers), req_ids=c.rids,
                 topk=[rq.k for rq in c.reqs], mode=mode, engine=engine, k_stride=c.k_stride,
@@ -305,11 +306,18 @@ def test_step_overlap_matches_serial_and_oracle(engine):
                 sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
                 block_table=[b.table for b in sets], scale=1.0 / math.sqrt(MULTI.d),
                 out=[outs[l] for l in layers], ws=sets[0].ws, compute_stream=compute,
-                copy_stream=copy_stream, want_stats=want_stats)
+                copy_stream=copy_stream, want_stats=want_stats, copy_stream2=copy2)
 
-        step(copy)
+        step(copy)  # odd layers on the context's own second copy stream
         torch.cuda.synchronize()
         overlapped = {l: outs[l].cpu().numpy().copy() for l in layers}
+        for o in outs.values():
+            o.fill_(float("nan"))
+        step(copy, copy2=torch.cuda.Stream())  # the caller's second copy stream
+        torch.cuda.synchronize()
+        for l in layers:
+            assert np.array_equal(outs[l].cpu().numpy().view(np.uint32),
+                                  overlapped[l].view(np.uint32)), l
         stats = step(compute, want_stats=True)  # serial: one stream
         torch.cuda.synchronize()
         for l in layers:
@@ -501,6 +509,32 @@ def test_error_paths_on_device():
         kv.kvoff_select(c.ctx, 0, [], c.q[0], c.digest[0], c.nb_max, [], kv.KVOFF_SOLOHEAD,
                         bufs.scores, bufs.sel_idx, bufs.sel_cnt, 8)
         torch.cuda.synchronize()
+    finally:
+        H.destroy(c)
+
+
+def test_attention_mass_error_paths():
+    H.log("[mass errors]")
+    s = synth.spec(1, ctx=512, k=8, hot=2)
+    c, sl = _case(s, [0])
+    try:
+        bufs = H.make_buffers(c, kv.KVOFF_SOLOHEAD)
+        mass = torch.empty((c.B, s.Hq), dtype=torch.float64, device="cuda")
+        args = (c.q[0], bufs.sel_idx, bufs.sel_cnt, c.k_stride, 0.1, mass)
+        with pytest.raises(kv.KvoffError) as e:  # unknown mode
+            kv.kvoff_attention_mass(c.ctx, 0, c.rids, 9, *args)
+        assert e.value.status == kv.KVOFF_EINVAL
+        with pytest.raises(kv.KvoffError) as e:  # layer outside the store
+            kv.kvoff_attention_mass(c.ctx, 1, c.rids, kv.KVOFF_SOLOHEAD, *args)
+        assert e.value.status == kv.KVOFF_ERANGE
+        with pytest.raises(kv.KvoffError) as e:  # unknown request
+            kv.kvoff_attention_mass(c.ctx, 0, [7], kv.KVOFF_SOLOHEAD, *args)
+        assert e.value.status == kv.KVOFF_ESTATE
+        with pytest.raises(kv.KvoffError) as e:  # k_stride < 1
+            kv.kvoff_attention_mass(c.ctx, 0, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], bufs.sel_idx,
+                                    bufs.sel_cnt, 0, 0.1, mass)
+        assert e.value.status == kv.KVOFF_EINVAL
+        kv.kvoff_attention_mass(c.ctx, 0, [], kv.KVOFF_SOLOHEAD, *args)  # empty batch: no-op
     finally:
         H.destroy(c)
 
