@@ -39,9 +39,9 @@ METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM 
 # workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
 # and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
 # the recall source it was taken with: reported as null once that changes.
-GATHER_PMC = {"workload": (2, 4), "fetch_kib": 65661.21, "write_kib": 131076.03,
+GATHER_PMC = {"workload": (2, 4), "fetch_kib": 65609.36, "write_kib": 131076.04,
               "fetch_scale": 1.9999, "write_scale": 1.0000,
-              "recall_src_sha256": "755b325f33a61e503127bc41acbc936143dcebe74ff8d43e1b0207a31c08a6cb"}
+              "recall_src_sha256": "6c1edea4033f55cfd722e363f8de81192f8a57bd65049463bf93884698783cfc"}
 
 
 def gather_traffic_bytes(config, layers):
@@ -246,17 +246,23 @@ def fragmentation_report(args):
 
 
 def admission_report(args):
-    """IO-adaptive admission on the batch-8 decode step shape: measure the
-    link utilisation of an overlapped multi-layer step, let the policy pick
-    the layers to keep in HBM, pin them, and measure again."""
+    """IO-adaptive admission as a control loop on the batch-8 decode step
+    shape (8 rotating layers of the 32-layer workload, HBM budget for 4 of
+    them).  Each round runs a window of steps, measures the link utilisation
+    (recalled bytes / (wall time x measured link peak)), asks the policy for
+    the resident layers and pins or releases layers to match.  The first
+    rounds issue steps back to back (the link saturates); the later ones pace
+    the steps at four times the saturated step time, as a lightly loaded
+    server would, so the utilisation drops and layers are handed back."""
     L = args.layers if args.layers != 4 else 8
+    budget = L // 2
     sp = synth.spec(3, L=L)
     reqs = synth.request_draws(sp)
     B = len(reqs)
     layers = list(range(L))
     nb_tot = sum(rq.nb for rq in reqs)
     case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
-                        layers, reqs, keep=lambda l, r: False, extra_slots=nb_tot * L)
+                        layers, reqs, keep=lambda l, r: False, extra_slots=nb_tot * budget)
     mode, engine = kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY
     sets = [H.make_buffers(case, mode) for _ in range(2)]
     outs = [torch.empty_like(sets[0].out) for _ in layers]
@@ -277,40 +283,68 @@ def admission_report(args):
             pool_slot=slot, pool_stride=case.nb_max, compute_stream=compute, copy_stream=copy,
             want_stats=want_stats)
 
-    def timed(n=6):
-        step()
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for _ in range(n):
-            step()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t) / n
-
-    st = step(want_stats=True)
-    sec = timed()
     copy_peak, _ = link_peaks(case)
-    util = st["bytes"] / sec / (copy_peak * 1e9)
     policy = kv.kvoff_admission_defaults()
+    policy.max_resident = budget
     resident = np.zeros(L, np.uint8)
-    n_res = kv.kvoff_admission_plan(policy, util, resident)
-    first = case.extra_base
-    rec_bytes = kv.kvoff_record_bytes(case.ctx)
-    for l in np.flatnonzero(resident).tolist():
-        for r, rq in enumerate(reqs):
-            kv.kvoff_make_resident(case.ctx, l, case.rids[r], case.pool, case.n_slots, first,
-                                   hit[l][r], slot[l][r])
-            first += rq.nb
+    home = {}                          # resident layer -> its slot range index
+    free = list(range(budget))
+
+    def apply(plan):
+        for l in np.flatnonzero((resident == 1) & (plan == 0)).tolist():  # release first
+            for r in range(B):
+                kv.kvoff_release_resident(case.ctx, l, case.rids[r], hit[l][r], stream=compute)
+            free.append(home.pop(l))
+        for l in np.flatnonzero((plan == 1) & (resident == 0)).tolist():
+            k = free.pop(0)
+            home[l] = k
+            first = case.extra_base + k * nb_tot
+            for r, rq in enumerate(reqs):
+                kv.kvoff_make_resident(case.ctx, l, case.rids[r], case.pool, case.n_slots, first,
+                                       hit[l][r], slot[l][r], stream=compute)
+                first += rq.nb
+        resident[:] = plan
+        torch.cuda.synchronize()
+
+    def window(n, period_s=None):
+        st = step(want_stats=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            t = time.perf_counter()
+            step()
+            if period_s:
+                torch.cuda.synchronize()
+                left = period_s - (time.perf_counter() - t)
+                if left > 0:
+                    time.sleep(left)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return st["bytes"] * n / (wall * copy_peak * 1e9), wall / n, st["bytes"]
+
+    step()
     torch.cuda.synchronize()
-    st2 = step(want_stats=True)
-    sec2 = timed()
-    out = {"workload": f"{sp.name}: batch {B}, {L} layers, context {reqs[0].ctx}, top-{reqs[0].k}",
-           "link_utilization": round(util, 4), "policy": {"low": policy.low, "high": policy.high,
-                                                          "max_offload": policy.max_offload},
-           "resident_layers": np.flatnonzero(resident).tolist(),
-           "hbm_bytes_resident": int(n_res * nb_tot * rec_bytes),
-           "before": {"layer_steps_per_s": round(L / sec, 2), "recalled_bytes": st["bytes"]},
-           "after": {"layer_steps_per_s": round(L / sec2, 2), "recalled_bytes": st2["bytes"],
-                     "pool_hits": st2["pool_hits"]}}
+    _, sat_step_s, _ = window(4)
+    rounds = []
+    for rnd in range(8):
+        paced = rnd >= 4
+        util, step_s, recalled = window(6, 4 * sat_step_s if paced else None)
+        before = np.flatnonzero(resident).tolist()
+        plan = resident.copy()
+        kv.kvoff_admission_plan(policy, util, plan)
+        apply(plan)
+        row = {"round": rnd, "load": "paced at 4x the saturated step" if paced else "back to back",
+               "link_utilization": round(util, 4), "resident_before": before,
+               "layer_steps_per_s": round(L / step_s, 1), "recalled_bytes_per_step": recalled,
+               "resident_after": np.flatnonzero(resident).tolist()}
+        log(str(row))
+        rounds.append(row)
+    out = {"workload": f"{sp.name}: batch {B}, {L} rotating layers, context {reqs[0].ctx}, "
+                       f"top-{reqs[0].k}, overlapped kvoff_step",
+           "policy": {"low": policy.low, "high": policy.high, "max_offload": policy.max_offload,
+                      "step_layers": policy.step_layers, "max_resident": policy.max_resident},
+           "hbm_bytes_per_resident_layer": int(nb_tot * kv.kvoff_record_bytes(case.ctx)),
+           "link_peak_gbps": round(copy_peak, 2), "rounds": rounds}
     H.destroy(case)
     print(json.dumps(out), flush=True)
 

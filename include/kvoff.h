@@ -232,7 +232,7 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
  *   block_table_dev out: SoloHead [n_req][k_stride] slot of each rank;
  *                 headwise [n_req][Hkv][k_stride] slice index (slot*Hkv + g);
  *                 unused entries -1
- *   engine        KVOFF_ENGINE_ZEROCOPY or KVOFF_ENGINE_DMA
+ *   engine        KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA or KVOFF_ENGINE_STAGED
  *   stats         nullable; when given, filled after synchronising the stream
  * Errors: EINVAL, ERANGE (recall region past n_slots), ESTATE (layer of a
  * request not offloaded), EHIP. */
@@ -249,7 +249,10 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
  *   q_dev         [n_req][Hq][d]
  *   block_table_dev, sel_idx_dev, sel_cnt_dev, k_stride: as produced by
  *                 kvoff_recall / kvoff_select (sel_idx gives each entry's
- *                 block id, so a request's partial last block is masked)
+ *                 block id, so a request's partial last block is masked).
+ *                 Block ids outside a request and negative table entries
+ *                 are skipped; a table entry is otherwise trusted to lie in
+ *                 slot_pool_dev (the pool's size is not passed here).
  *   scale         logit scale (1/sqrt(d) for standard attention)
  *   out_dev       out: [n_req][Hq][d] fp32
  *   ws_dev        scratch of at least kvoff_workspace_size(ctx,
@@ -376,6 +379,8 @@ typedef struct kvoff_admission_policy {
   double high;         /* utilisation above which more layers are pinned (0.85) */
   double max_offload;  /* largest offloaded fraction of the layers (0.90)      */
   int32_t step_layers; /* layers pinned or released per decision (2)           */
+  int32_t max_resident; /* most layers the HBM budget holds (INT32_MAX: no cap);
+                           applied last, so it wins over the offload ceiling  */
 } kvoff_admission_policy;
 
 /* Fills *p with the defaults above. */
@@ -385,8 +390,9 @@ void kvoff_admission_defaults(kvoff_admission_policy* p);
  * link peak) over the last window.  resident [num_layers] is the current plan
  * on entry (1 = kept in HBM) and the new plan on return.  Layers are pinned
  * in the order 0, L-1, 1, L-2, ... and released in the reverse order; at
- * least ceil((1 - max_offload) * num_layers) stay resident.  *n_resident
- * receives the new count.  Pure host logic.  Errors: EINVAL. */
+ * least ceil((1 - max_offload) * num_layers) stay resident, and at most
+ * max_resident.  *n_resident receives the new count.  Pure host logic.
+ * Errors: EINVAL. */
 int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, double utilization,
                          uint8_t* resident, int32_t* n_resident);
 

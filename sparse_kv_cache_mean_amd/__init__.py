@@ -59,7 +59,8 @@ class kvoff_config(ctypes.Structure):
 
 class kvoff_admission_policy(ctypes.Structure):
     _fields_ = [("low", ctypes.c_double), ("high", ctypes.c_double),
-                ("max_offload", ctypes.c_double), ("step_layers", ctypes.c_int32)]
+                ("max_offload", ctypes.c_double), ("step_layers", ctypes.c_int32),
+                ("max_resident", ctypes.c_int32)]
 
 
 class kvoff_stats(ctypes.Structure):

@@ -6,6 +6,7 @@
 // 85%), the 90% offload ceiling and that the first and last layers are the
 // ones kept; the pinning order between them, the step of two layers per
 // decision and the rounding of the floor are this library's reading.
+#include <climits>
 #include <cmath>
 #include <vector>
 
@@ -45,6 +46,7 @@ void kvoff_admission_defaults(kvoff_admission_policy* p) {
   p->high = 0.85;
   p->max_offload = 0.90;
   p->step_layers = 2;
+  p->max_resident = INT32_MAX;
 }
 
 int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, double utilization,
@@ -52,7 +54,7 @@ int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, do
   if (!p || !resident || !n_resident || num_layers < 1)
     return fail(KVOFF_EINVAL, "admission: NULL argument or num_layers < 1");
   if (!(p->low >= 0.0 && p->low <= p->high) || !(p->max_offload >= 0.0 && p->max_offload <= 1.0) ||
-      p->step_layers < 1 || !(utilization >= 0.0))
+      p->step_layers < 1 || p->max_resident < 0 || !(utilization >= 0.0))
     return fail(KVOFF_EINVAL, "admission: bad policy or utilization");
   const std::vector<int> order = pin_order(num_layers);
   int cur = 0;
@@ -65,6 +67,7 @@ int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, do
     want = cur - p->step_layers;
   if (want < floor_res) want = floor_res;
   if (want > num_layers) want = num_layers;
+  if (want > p->max_resident) want = p->max_resident;  // the HBM budget wins
   for (int i = 0; i < num_layers; ++i) resident[i] = 0;
   for (int i = 0; i < want; ++i) resident[order[i]] = 1;
   *n_resident = want;

@@ -97,8 +97,10 @@ __device__ __forceinline__ void write_table_and_count(const GatherArgs& a, int64
       bool cont = false;
       if (!a.hw && it.i > 0) {
         const int pb = a.sel_idx[item - 1];
-        const bool phit = a.pool_hit && a.pool_hit[(int64_t)it.r * a.pool_stride + pb];
-        cont = pb == it.b - 1 && !phit;
+        if (pb >= 0 && pb == it.b - 1) {  // then pb is inside the request too
+          const bool phit = a.pool_hit && a.pool_hit[(int64_t)it.r * a.pool_stride + pb];
+          cont = !phit;
+        }
       }
       if (!cont) atomicAdd(&a.counters[3], 1ull);
     }

@@ -14,6 +14,7 @@ def _plan(p, u, res):
 def test_defaults_follow_the_guide():
     p = kv.kvoff_admission_defaults()
     assert (p.low, p.high, p.max_offload, p.step_layers) == (0.5, 0.85, 0.9, 2)
+    assert p.max_resident == 2**31 - 1  # no HBM cap unless the caller sets one
 
 
 def test_saturated_link_pins_first_and_last_layers_inward():
@@ -57,7 +58,20 @@ def test_odd_layer_count_meets_in_the_middle():
     assert order == [0, 4, 1, 3, 2]
 
 
-@pytest.mark.parametrize("bad", [dict(low=0.9, high=0.5), dict(max_offload=1.5), dict(step_layers=0)])
+def test_hbm_budget_caps_residency_and_wins_over_the_floor():
+    p = kv.kvoff_admission_defaults()
+    p.max_resident = 3
+    res = np.zeros(8, np.uint8)
+    assert _plan(p, 0.99, res) == (2, [0, 7])
+    assert _plan(p, 0.99, res) == (3, [0, 1, 7])   # +2 would be 4: capped at 3
+    assert _plan(p, 0.99, res) == (3, [0, 1, 7])
+    p.max_resident = 0                               # no HBM to spare
+    res = np.zeros(32, np.uint8)
+    assert _plan(p, 0.1, res) == (0, [])             # below the floor of 4: the budget wins
+
+
+@pytest.mark.parametrize("bad", [dict(low=0.9, high=0.5), dict(max_offload=1.5), dict(step_layers=0),
+                                 dict(max_resident=-1)])
 def test_bad_policy_is_rejected(bad):
     p = kv.kvoff_admission_defaults()
     for k, v in bad.items():
