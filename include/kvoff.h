@@ -332,14 +332,18 @@ typedef struct kvoff_step_args {
   void* copy_stream2;
 } kvoff_step_args;
 
-/* Where the compute stream's time went in one kvoff_step, from HIP timing
- * events on that stream (milliseconds). */
+/* Where the time went in one kvoff_step, from HIP timing events
+ * (milliseconds): the first four on the compute stream, recall_ms on the copy
+ * streams around each recall call (one per layer, or per request group). */
 typedef struct kvoff_step_timing {
   double step_ms;              /* first select launched -> last attention done */
   double compute_wait_ms;      /* compute stream idle, waiting for recalls      */
   double mean_request_done_ms; /* mean over requests of step start -> the end
                                   of that request's last-layer attention       */
   double max_request_done_ms;  /* the same, latest request                     */
+  double recall_ms;            /* sum over the step's recall calls of their
+                                  duration, from events on the copy streams   */
+  int64_t recalls;             /* number of those recall calls                 */
 } kvoff_step_timing;
 
 int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* args);

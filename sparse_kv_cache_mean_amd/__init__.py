@@ -96,10 +96,11 @@ class kvoff_step_args(ctypes.Structure):
 class kvoff_step_timing(ctypes.Structure):
     _fields_ = [("step_ms", ctypes.c_double), ("compute_wait_ms", ctypes.c_double),
                 ("mean_request_done_ms", ctypes.c_double),
-                ("max_request_done_ms", ctypes.c_double)]
+                ("max_request_done_ms", ctypes.c_double), ("recall_ms", ctypes.c_double),
+                ("recalls", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
-        return {k: float(getattr(self, k)) for k, _ in self._fields_}
+        return {k: (int if k == "recalls" else float)(getattr(self, k)) for k, _ in self._fields_}
 
 
 _lib = None

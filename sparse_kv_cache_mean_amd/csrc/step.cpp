@@ -113,11 +113,12 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     ctx->ev_group.push_back(e);
   }
   // timing events (on request): the step's start, then per (layer, group)
-  // before the wait for its recall, after it, and after its attention
+  // before the wait for its recall, after it, after its attention, and on
+  // the copy stream before and after its recall call
   const size_t NG = groups.size();
-  auto tev = [&](int li, size_t gi, int k) { return ctx->ev_timing[1 + ((size_t)li * NG + gi) * 3 + k]; };
+  auto tev = [&](int li, size_t gi, int k) { return ctx->ev_timing[1 + ((size_t)li * NG + gi) * 5 + k]; };
   if (A->timing) {
-    while (ctx->ev_timing.size() < 1 + 3 * (size_t)L * NG) {
+    while (ctx->ev_timing.size() < 1 + 5 * (size_t)L * NG) {
       hipEvent_t e;
       KVOFF_HIP(hipEventCreate(&e));
       ctx->ev_timing.push_back(e);
@@ -134,6 +135,7 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
       const Group& g = groups[gi];
       const int64_t sel_off = (int64_t)g.r0 * sets * A->k_stride;
       kvoff_stats st_l;
+      if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 3), xs));
       int st = kvoff_recall(
           ctx, A->layer_begin + li, g.n, A->req_ids + g.r0, A->mode, A->sel_idx_dev[buf] + sel_off,
           A->sel_cnt_dev[buf] + g.r0, A->k_stride,
@@ -143,6 +145,7 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
           A->recall_base_slot[buf] + (int64_t)g.r0 * A->k_stride, A->block_table_dev[buf] + sel_off,
           A->engine, A->stats ? &st_l : nullptr, xs);
       if (st) return st;
+      if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 4), xs));
       if (A->stats) {
         A->stats->selected += st_l.selected;
         A->stats->pool_hits += st_l.pool_hits;
@@ -189,6 +192,10 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
       for (size_t gi = 0; gi < NG; ++gi) {
         KVOFF_HIP(hipEventElapsedTime(&ms, tev(li, gi, 0), tev(li, gi, 1)));
         T.compute_wait_ms += ms;
+        KVOFF_HIP(hipEventSynchronize(tev(li, gi, 4)));
+        KVOFF_HIP(hipEventElapsedTime(&ms, tev(li, gi, 3), tev(li, gi, 4)));
+        T.recall_ms += ms;
+        ++T.recalls;
       }
     for (size_t gi = 0; gi < NG; ++gi) {  // requests finish with their last layer
       KVOFF_HIP(hipEventElapsedTime(&ms, ctx->ev_timing[0], tev(L - 1, gi, 2)));

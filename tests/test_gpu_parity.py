@@ -422,6 +422,8 @@ def test_step_groups_with_resident_requests():
             assert 0 <= t["compute_wait_ms"] < t["step_ms"]
             if grp == 0:
                 assert t["mean_request_done_ms"] == t["max_request_done_ms"]
+            n_groups = 1 if grp == 0 else -(-c.B // grp)
+            assert t["recalls"] == len(layers) * n_groups and t["recall_ms"] > 0
         want_items = sum(min(reqs[r].k, reqs[r].nb) for l in layers for r in range(c.B)
                          if r not in pinned[l])
         for grp in (0, 1, 2):
