@@ -218,7 +218,7 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   // one worker task per 1 MiB of staging (kStageChunk / 4): it copies every
   // piece, or part of a piece, that lands in its range.  A chunk's bulk copy
   // is issued once its four tasks are done.
-  constexpr size_t kTask = kStageChunk / 4;
+  constexpr size_t kTask = kStageChunk / 4;  // measured: 512 KiB, 2 MiB, 4 MiB all slower
   const size_t n_chunks = (total + kStageChunk - 1) / kStageChunk;
   const size_t n_tasks = (total + kTask - 1) / kTask;
   ChunkDone done;
