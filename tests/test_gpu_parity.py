@@ -263,6 +263,39 @@ def test_attention_mass_matches_oracle(which):
         H.destroy(c)
 
 
+def test_very_long_context_takes_the_streaming_topk():
+    """More than 16384 blocks in one request: the top-k re-reads the scores
+    each pass instead of holding them in registers; k above 128 uses four
+    blocks per attention wave."""
+    s = synth.spec(1, B=2, ctx=300_000, k=300, hot=40)  # bs 16: 18750 blocks per request
+    H.log(f"[long context] {s.ctx} tokens, {-(-s.ctx // s.bs)} blocks, k {s.k}")
+    c, sl = _case(s, [0])
+    try:
+        assert c.nb_max > 16384
+        stats, err = _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+        H.log(f"  stats {stats} attention err {err}")
+    finally:
+        H.destroy(c)
+
+
+def test_largest_batch_and_one_past_it():
+    """KVOFF_MAX_BATCH (128) requests in one call, mixed short contexts; 129
+    is rejected before anything is enqueued."""
+    s = synth.spec(4, B=kv.KVOFF_MAX_BATCH, ctx_range=(40, 400), k_frac_range=(0.1, 0.6), hot=0)
+    H.log(f"[max batch] {s.B} requests")
+    c, sl = _case(s, [0])
+    try:
+        _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+        bufs = H.make_buffers(c, kv.KVOFF_SOLOHEAD)
+        with pytest.raises(kv.KvoffError) as e:
+            kv.kvoff_select(c.ctx, 0, c.rids + [c.rids[0]], c.q[0], c.digest[0], c.nb_max,
+                            [1] * (s.B + 1), kv.KVOFF_SOLOHEAD, bufs.scores, bufs.sel_idx,
+                            bufs.sel_cnt, c.k_stride)
+        assert e.value.status == kv.KVOFF_ERANGE
+    finally:
+        H.destroy(c)
+
+
 def test_degenerate_sizes():
     """k >= nb (take every block), k = 1, one-token and one-block contexts."""
     H.log("[degenerate]")
