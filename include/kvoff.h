@@ -292,8 +292,8 @@ typedef struct kvoff_step_args {
   const void* const* q_dev;          /* [layers] -> [n_req][Hq][d]            */
   const float* const* digest_dev;    /* [layers] -> digests (see kvoff_select) */
   int64_t digest_stride;
-  const uint8_t* const* pool_hit_dev;  /* nullable; [layers] -> hit maps     */
-  const int32_t* const* pool_slot_dev; /* nullable; [layers] -> pool slots   */
+  const uint8_t* const* pool_hit_dev;  /* nullable; [layers] -> hit maps; a  */
+  const int32_t* const* pool_slot_dev; /* layer's pair may be NULL (no pool) */
   int64_t pool_stride;
   void* slot_pool_dev;
   int64_t n_slots;

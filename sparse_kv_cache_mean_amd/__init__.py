@@ -281,7 +281,9 @@ def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[
     the compute-stream timing under "timing" (want_timing)."""
     n_layers = layer_end - layer_begin
     ids, tk = _i32_array(req_ids), _i32_array(topk)
-    arr = lambda ts: (_vp * max(n_layers, 1))(*[_ptr(t) for t in ts])
+    # one pointer per layer, NULL-padded: the library checks the layer range
+    # and rejects missing per-layer buffers itself
+    arr = lambda ts: (_vp * max(n_layers, len(ts), 1))(*[_ptr(t) for t in ts])
     a = kvoff_step_args()
     a.layer_begin, a.layer_end, a.n_req = layer_begin, layer_end, len(req_ids)
     a.req_ids = ctypes.cast(ids, _vp)

@@ -49,6 +49,16 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
   for (int i = 0; i < 2; ++i)
     if (!A->scores_dev[i] || !A->sel_idx_dev[i] || !A->sel_cnt_dev[i] || !A->block_table_dev[i])
       return fail(KVOFF_EINVAL, "buffer set %d has a NULL buffer", i);
+  // every per-layer pointer up front, so a bad one never leaves a step half enqueued
+  for (int li = 0; li < L; ++li) {
+    if (!A->q_dev[li] || !A->digest_dev[li] || !A->out_dev[li])
+      return fail(KVOFF_EINVAL, "layer %d: NULL q, digest or out", A->layer_begin + li);
+    if (A->pool_hit_dev && (!A->pool_hit_dev[li] != !(A->pool_slot_dev && A->pool_slot_dev[li])))
+      return fail(KVOFF_EINVAL, "layer %d: pool hit and slot maps must both be given or both NULL",
+                  A->layer_begin + li);
+  }
+  if (!A->pool_hit_dev != !A->pool_slot_dev)
+    return fail(KVOFF_EINVAL, "pool_hit_dev and pool_slot_dev must both be given or both NULL");
   if (L > 1 && A->recall_base_slot[0] == A->recall_base_slot[1] && A->copy_stream != A->compute_stream)
     return fail(KVOFF_EINVAL, "overlapped layers need two distinct recall regions");
 
@@ -129,6 +139,9 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
 
   auto recall_l = [&](int li) -> int {
     const int buf = li & 1;
+    // this layer's pool maps (a layer may have none)
+    const uint8_t* hit_l = A->pool_hit_dev ? A->pool_hit_dev[li] : nullptr;
+    const int32_t* slot_l = A->pool_slot_dev ? A->pool_slot_dev[li] : nullptr;
     hipStream_t xs = xs_of(li);
     KVOFF_HIP(hipStreamWaitEvent(xs, ctx->ev_sel[buf], 0));
     for (int gi : order_for(li)) {
@@ -139,8 +152,8 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
       int st = kvoff_recall(
           ctx, A->layer_begin + li, g.n, A->req_ids + g.r0, A->mode, A->sel_idx_dev[buf] + sel_off,
           A->sel_cnt_dev[buf] + g.r0, A->k_stride,
-          A->pool_hit_dev ? A->pool_hit_dev[li] + (int64_t)g.r0 * A->pool_stride : nullptr,
-          A->pool_slot_dev ? A->pool_slot_dev[li] + (int64_t)g.r0 * A->pool_stride : nullptr,
+          hit_l ? hit_l + (int64_t)g.r0 * A->pool_stride : nullptr,
+          slot_l ? slot_l + (int64_t)g.r0 * A->pool_stride : nullptr,
           A->pool_stride, A->slot_pool_dev, A->n_slots,
           A->recall_base_slot[buf] + (int64_t)g.r0 * A->k_stride, A->block_table_dev[buf] + sel_off,
           A->engine, A->stats ? &st_l : nullptr, xs);

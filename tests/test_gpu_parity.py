@@ -574,6 +574,63 @@ def test_attention_mass_error_paths():
         H.destroy(c)
 
 
+def test_step_error_paths():
+    """kvoff_step rejects bad layer ranges, shared recall regions when
+    overlapping, unknown requests and NULL buffers (also a later layer's)
+    before enqueuing any work."""
+    H.log("[step errors]")
+    layers = list(range(MULTI.L))
+    c, sl = _case(MULTI, layers)
+    try:
+        sets = [H.make_buffers(c, kv.KVOFF_SOLOHEAD) for _ in range(2)]
+        outs = [torch.empty((c.B, MULTI.Hq, MULTI.d), dtype=torch.float32, device="cuda")
+                for _ in layers]
+        compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
+
+        def step(**kw):
+            args = dict(layer_begin=0, layer_end=len(layers), req_ids=c.rids,
+                        topk=[rq.k for rq in c.reqs], mode=kv.KVOFF_SOLOHEAD,
+                        engine=kv.KVOFF_ENGINE_ZEROCOPY, k_stride=c.k_stride,
+                        q=[c.q[l] for l in layers], digest=[c.digest[l] for l in layers],
+                        digest_stride=c.nb_max, slot_pool=c.pool, n_slots=c.n_slots,
+                        recall_base_slot=c.recall_base, scores=[b.scores for b in sets],
+                        sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
+                        block_table=[b.table for b in sets], scale=0.1, out=outs, ws=sets[0].ws,
+                        compute_stream=compute, copy_stream=copy)
+            args.update(kw)
+            return kv.kvoff_step(c.ctx, **args)
+
+        for kw, status in ((dict(layer_end=len(layers) + 1), kv.KVOFF_ERANGE),
+                           (dict(layer_begin=-1), kv.KVOFF_ERANGE),
+                           (dict(recall_base_slot=(0, 0)), kv.KVOFF_EINVAL),
+                           (dict(req_ids=[c.rids[0], 99]), kv.KVOFF_ESTATE),
+                           (dict(q=[c.q[l] for l in layers[:-1]] + [None]), kv.KVOFF_EINVAL)):
+            with pytest.raises(kv.KvoffError) as e:
+                step(**kw)
+            assert e.value.status == status, kw
+        with pytest.raises(kv.KvoffError) as e:  # a hit map without its slot map
+            step(pool_hit=[None] + [torch.zeros((c.B, c.nb_max), dtype=torch.uint8, device="cuda")]
+                 * (len(layers) - 1), pool_slot=[None] * len(layers), pool_stride=c.nb_max)
+        assert e.value.status == kv.KVOFF_EINVAL
+        # one stream for both roles may share a recall region (serial order)
+        step(recall_base_slot=(0, 0), copy_stream=compute)
+        step(layer_end=0)  # an empty layer range is a no-op
+        # maps for some layers only: the others recall everything
+        step()
+        torch.cuda.synchronize()
+        ref = [o.cpu().numpy().copy() for o in outs]
+        hits = [None] + [torch.zeros((c.B, c.nb_max), dtype=torch.uint8, device="cuda")
+                         for _ in layers[1:]]
+        slots = [None] + [torch.full((c.B, c.nb_max), -1, dtype=torch.int32, device="cuda")
+                          for _ in layers[1:]]
+        step(pool_hit=hits, pool_slot=slots, pool_stride=c.nb_max)
+        torch.cuda.synchronize()
+        for l in layers:
+            assert np.array_equal(outs[l].cpu().numpy().view(np.uint32), ref[l].view(np.uint32)), l
+    finally:
+        H.destroy(c)
+
+
 def test_recall_before_offload_is_rejected():
     H.log("[errors] recall before offload")
     ctx = kv.kvoff_create(num_layers=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
