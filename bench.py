@@ -10,7 +10,7 @@ from the previous one.  Inputs are synthetic (seeded generator, no gap
 conditioning: that only matters for parity checks) and are resident in HBM /
 the pinned store before timing starts.
 
-Prints one JSON line.  `--gpus N` with N > 1 exits: this build measures one GPU.
+Prints one JSON line.  `--gpus N` with N > 1 exits: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -39,14 +39,14 @@ METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM 
 # workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
 # and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
 # the recall source it was taken with: reported as null once that changes.
-GATHER_PMC = {"workload": (2, 4), "fetch_kib": 65609.36, "write_kib": 131076.04,
+GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65609.36, "write_kib": 131076.04,
               "fetch_scale": 1.9999, "write_scale": 1.0000,
               "recall_src_sha256": "6c1edea4033f55cfd722e363f8de81192f8a57bd65049463bf93884698783cfc"}
 
 
-def gather_traffic_bytes(config, layers):
+def gather_traffic_bytes(workload, layers):
     import hashlib
-    if (config, layers) != GATHER_PMC["workload"]:
+    if (workload, layers) != GATHER_PMC["workload"]:
         return None
     src = os.path.join(ROOT, "sparse_kv_cache_mean_amd", "csrc", "recall.hip")
     with open(src, "rb") as f:
@@ -67,7 +67,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=40)
     p.add_argument("--warmup", type=int, default=8)
-    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--workload", default="llama3-8b-layer",
+                   choices=[w.name for w in synth.WORKLOADS.values()])
+    p.add_argument("--config", type=int, default=None, help=argparse.SUPPRESS)  # by number
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--engine", choices=["zerocopy", "dma", "staged"], default="zerocopy")
     p.add_argument("--host-mem", choices=["coherent", "noncoherent"], default="coherent")
@@ -76,11 +78,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-overlap", action="store_true",
-                   help="skip the overlapped kvoff_step measurement (for clean kernel traces)")
+                   help="time the serial order on one stream as the value instead of "
+                        "kvoff_step (every gather then runs alone: clean kernel traces)")
     p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass", "decode32"], default=None,
                    help="instead of the bench line: fragmentation = recall of the "
                         "headwise-vs-SoloHead workload with every engine; admission = the "
-                        "multi-layer step before and after one admission decision; groups = "
+                        "admission policy as a control loop over the multi-layer step; groups = "
                         "interruptible per-request scheduling on the variable-recall layer; "
                         "mass = attention mass kept and recall volume of every selection mode; "
                         "decode32 = the overlapped 32-layer decode step")
@@ -578,7 +581,7 @@ def main():
         return mass_report(args)
     if args.report == "decode32":
         return decode32_report(args)
-    sp = synth.spec(args.config, L=args.layers)
+    sp = synth.spec(args.config if args.config else args.workload, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)
     layers = list(range(args.layers))
@@ -733,7 +736,7 @@ def main():
                        2: "CPU gather + bulk hipMemcpyAsync"}[engine],
             "bound": "pcie", "achieved": round(roof_gbps, 2), "peak": PCIE_PEAK_GBPS,
             "unit": "GB/s", "frac": round(roof_gbps / PCIE_PEAK_GBPS, 4),
-            "traffic": gather_traffic_bytes(args.config, args.layers)
+            "traffic": gather_traffic_bytes(sp.name, args.layers)
             if engine == kv.KVOFF_ENGINE_ZEROCOPY else None,
             "traffic_note": "counter bytes per launch: host-link fetches + HBM writes "
                             "(a copy moves each byte twice)",

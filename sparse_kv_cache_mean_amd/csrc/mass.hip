@@ -1,7 +1,7 @@
 // mass.hip - attention mass a block selection keeps (kvoff_attention_mass).
 //
 // The guide ("PulseInfer Guide", aiFetchly, section "SoloHead Sparse
-// Selection", attention mass preservation) judges a shared block set by the
+// Selection", attention mass preservation) assesses a shared block set by the
 // share of the attention weight it keeps compared with per-head sets.  For
 // each request r and query head h (KV head g = floor(h/G)):
 //   z_t    = scale * <q_h, K_t[g]> over all valid tokens t of the context

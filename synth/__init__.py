@@ -175,26 +175,33 @@ class Spec:
         return 2 * self.Hkv * self.bs * self.d * self.es
 
 
-def _c(cfg_id: int) -> int:
-    return 1000 + cfg_id
+def _seed(number: int) -> int:
+    return 1000 + number
 
 
-CONFIGS = {
+# the five workloads, by number; each also has a name
+WORKLOADS = {
     1: Spec("tiny", B=1, L=1, Hq=8, Hkv=2, d=128, bs=16, dtype=F16, ctx=4096, k=32, hot=32,
-            seed=_c(1)),
+            seed=_seed(1)),
     2: Spec("llama3-8b-layer", B=16, L=1, Hq=32, Hkv=8, d=128, bs=32, dtype=BF16, ctx=32768,
-            k=64, hot=51, seed=_c(2)),
+            k=64, hot=51, seed=_seed(2)),
     3: Spec("llama3-8b-32layer", B=8, L=32, Hq=32, Hkv=8, d=128, bs=32, dtype=BF16, ctx=32768,
-            k=64, hot=51, seed=_c(3)),
+            k=64, hot=51, seed=_seed(3)),
     4: Spec("llama3-70b-variable", B=32, L=1, Hq=64, Hkv=8, d=128, bs=32, dtype=BF16,
-            ctx_range=(8192, 131072), k_frac_range=(0.02, 0.15), hot_runs=True, seed=_c(4)),
+            ctx_range=(8192, 131072), k_frac_range=(0.02, 0.15), hot_runs=True, seed=_seed(4)),
     5: Spec("headwise-vs-solohead", B=16, L=1, Hq=32, Hkv=8, d=128, bs=32, dtype=BF16,
-            ctx=32768, k=64, hot=51, pool_frac=0.25, headwise=True, seed=_c(5)),
+            ctx=32768, k=64, hot=51, pool_frac=0.25, headwise=True, seed=_seed(5)),
 }
 
 
-def spec(cfg_id: int, **overrides) -> Spec:
-    return replace(CONFIGS[cfg_id], **overrides)
+def spec(workload, **overrides) -> Spec:
+    """The workload by number (1-5) or name, with fields overridden."""
+    if isinstance(workload, str):
+        matches = [w for w in WORKLOADS.values() if w.name == workload]
+        if not matches:
+            raise KeyError(f"no workload named {workload!r}")
+        return replace(matches[0], **overrides)
+    return replace(WORKLOADS[workload], **overrides)
 
 
 @dataclass
