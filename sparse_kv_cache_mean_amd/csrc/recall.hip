@@ -16,9 +16,13 @@
 //            consecutive missing blocks and issues one hipMemcpyAsync per
 //            run (per slice when headwise) on the stream, which the copy
 //            engines execute.
+// A third engine, STAGED (the guide's CPU gather into pinned staging plus
+// bulk copies), is in staged.cpp.  Every engine ignores a selected block id
+// outside its request, as if the entry were unused.
 //
 // Slot layout: rank i of request r goes to slot base + r*k_stride + i, so a
 // run of consecutive block ids is contiguous in the store and in the pool.
+#include <algorithm>
 #include <cstdlib>
 #include <vector>
 
@@ -289,12 +293,17 @@ int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_sta
   for (int ri = 0; ri < b.n; ++ri) {
     const ReqHost& rq = ctx->reqs[b.id[ri]];
     const uint8_t* rec_l = ctx->store + (size_t)(rq.rec_base + (int64_t)r.layer * rq.nb) * ctx->rec_bytes;
-    const int K = cnt[ri];
+    const int K = std::min(cnt[ri], r.k_stride);
     for (int g = 0; g < sets; ++g) {
       const int32_t* s = sel.data() + ((size_t)ri * sets + g) * r.k_stride;
       auto is_hit = [&](int32_t blk) { return r.pool_hit && hit[(size_t)ri * r.pool_stride + blk]; };
+      auto valid = [&](int32_t blk) { return blk >= 0 && blk < rq.nb; };
       int i = 0;
       while (i < K) {
+        if (!valid(s[i])) {  // an id outside the request: an unused entry
+          ++i;
+          continue;
+        }
         ++n_selected;
         if (is_hit(s[i])) {
           ++n_hits;
@@ -303,7 +312,7 @@ int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_sta
         }
         int j = i + 1;
         if (!hw)
-          while (j < K && s[j] == s[j - 1] + 1 && !is_hit(s[j])) ++j;
+          while (j < K && valid(s[j]) && s[j] == s[j - 1] + 1 && !is_hit(s[j])) ++j;
         n_selected += j - i - 1;
         const int64_t slot = r.recall_base_slot + (int64_t)ri * r.k_stride + i;
         const uint8_t* src = rec_l + (size_t)s[i] * ctx->rec_bytes + (hw ? (size_t)g * item : 0);

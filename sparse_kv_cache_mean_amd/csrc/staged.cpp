@@ -179,11 +179,11 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
     for (int g = 0; g < sets; ++g) {
       const size_t row = ((size_t)ri * sets + g) * r.k_stride;
       for (int i = 0; i < r.k_stride; ++i) {
-        if (i >= K) {
+        const int32_t blk = i < K ? sel[row + i] : -1;
+        if (blk < 0 || blk >= rq.nb) {  // unused entry (or an id outside the request)
           table[row + i] = -1;
           continue;
         }
-        const int32_t blk = sel[row + i];
         ++n_selected;
         if (r.pool_hit && hit[(size_t)ri * r.pool_stride + blk]) {
           const int64_t ps = pslot[(size_t)ri * r.pool_stride + blk];

@@ -574,6 +574,45 @@ def test_attention_mass_error_paths():
         H.destroy(c)
 
 
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
+def test_out_of_range_block_ids_are_unused_entries(engine):
+    """A selection entry outside its request (too large or negative) is
+    treated as unused by every recall engine and by the attention: no bytes
+    move for it, its table entry is -1, and attention covers the rest."""
+    H.log(f"[bad ids] engine {engine}")
+    s = synth.spec(2, B=2, ctx=3000, k=12, hot=5)
+    c, sl = _case(s, [0])
+    try:
+        bufs = H.make_buffers(c, kv.KVOFF_SOLOHEAD)
+        kv.kvoff_select(c.ctx, 0, c.rids, c.q[0], c.digest[0], c.nb_max, [rq.k for rq in c.reqs],
+                        kv.KVOFF_SOLOHEAD, bufs.scores, bufs.sel_idx, bufs.sel_cnt, c.k_stride)
+        torch.cuda.synchronize()
+        nb = [rq.nb for rq in c.reqs]
+        bad = {(0, 2): nb[0] + 5, (1, 0): -7}
+        for (r, i), v in bad.items():
+            bufs.sel_idx[r, 0, i] = v
+        st = kv.kvoff_recall(c.ctx, 0, c.rids, kv.KVOFF_SOLOHEAD, bufs.sel_idx, bufs.sel_cnt,
+                             c.k_stride, None, None, 0, c.pool, c.n_slots, c.recall_base[0],
+                             bufs.table, engine, want_stats=True)
+        kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, bufs.table,
+                               bufs.sel_idx, bufs.sel_cnt, c.k_stride, 1.0 / math.sqrt(s.d),
+                               bufs.out, bufs.ws)
+        torch.cuda.synchronize()
+        table = bufs.table.cpu().numpy()
+        for (r, i) in bad:
+            assert table[r, 0, i] == -1, (r, i)
+        K = sum(x.K for x in sl.values())
+        assert st["selected"] == K - len(bad) and st["items_recalled"] == K - len(bad)
+        got = bufs.out.cpu().numpy()
+        for r in range(c.B):
+            x = sl[(0, r)]
+            keep = np.array([b for i, b in enumerate(x.sel.tolist()) if (r, i) not in bad], np.int32)
+            ref = oracle.attend_f32(x.lr.q, x.lr.K, x.lr.V, s.dtype, s.bs, keep)
+            P.check_attention_close(got[r], ref, f"request {r}")
+    finally:
+        H.destroy(c)
+
+
 def test_step_error_paths():
     """kvoff_step rejects bad layer ranges, shared recall regions when
     overlapping, unknown requests and NULL buffers (also a later layer's)
