@@ -13,7 +13,9 @@
 //    them (item n of the call -> slot recall_base + n; headwise: slice
 //    recall_base*Hkv + n), so the attention reads them where they land.
 // The staging buffer and the block-table staging are reused by the next
-// call only after an event recorded behind the last copy has completed.
+// call only after an event recorded behind this call's last copy (the table
+// upload when nothing is recalled) has completed; the next call may run on
+// another stream, so the event, not stream order, protects them.
 #include <emmintrin.h>
 
 #include <algorithm>
@@ -204,6 +206,10 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   const size_t total = (size_t)n_items * item;
   KVOFF_HIP(hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream));
   if (total == 0) {
+    // the upload reads the block-table staging: the next call (possibly on
+    // another stream) waits for this event before rewriting it
+    KVOFF_HIP(hipEventRecord(ctx->ev_stage, stream));
+    ctx->ev_stage_pending = true;
     if (stats) {
       KVOFF_HIP(hipStreamSynchronize(stream));
       *stats = kvoff_stats{n_selected, n_hits, 0, 0, 0};

@@ -409,11 +409,14 @@ def test_step_request_groups_match_whole_batch(engine):
         H.destroy(c)
 
 
-def test_step_groups_with_resident_requests():
+@pytest.mark.parametrize("engine", [kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED])
+def test_step_groups_with_resident_requests(engine):
     """Request groups reordered by residency (resident groups first, a
     different order per layer) still give the whole-batch bits, and pinned
-    (layer, request) pairs recall nothing."""
-    H.log("[step groups] resident requests")
+    (layer, request) pairs recall nothing.  With groups of one request, a
+    resident request's recall moves nothing at all (for the staged engine:
+    only its block table goes up), on alternating copy streams."""
+    H.log(f"[step groups] resident requests, engine {engine}")
     s = RAGGED_LAYERS
     layers = [0, 1]
     reqs, sl = _slices(s, layers)
@@ -438,7 +441,7 @@ def test_step_groups_with_resident_requests():
             outs = [torch.full((c.B, s.Hq, s.d), float("nan"), device="cuda") for _ in layers]
             st = kv.kvoff_step(
                 c.ctx, layer_begin=0, layer_end=2, req_ids=c.rids, topk=[rq.k for rq in reqs],
-                mode=mode, engine=kv.KVOFF_ENGINE_ZEROCOPY, k_stride=c.k_stride,
+                mode=mode, engine=engine, k_stride=c.k_stride,
                 q=[c.q[l] for l in layers], digest=[c.digest[l] for l in layers],
                 digest_stride=c.nb_max, slot_pool=c.pool, n_slots=c.n_slots,
                 recall_base_slot=c.recall_base, scores=[b.scores for b in sets],
