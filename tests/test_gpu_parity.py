@@ -296,6 +296,22 @@ def test_largest_batch_and_one_past_it():
         H.destroy(c)
 
 
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("bs", [16, 32])
+def test_dtype_and_block_size_grid(dtype, bs):
+    """Every (storage type, block size) pair of the kernels, SoloHead and
+    headwise, with a ragged last block."""
+    s = synth.spec(2, B=2, dtype=dtype, bs=bs, ctx=2500, k=14, hot=6, headwise=True)
+    H.log(f"[dtype/bs] dtype {dtype} bs {bs}")
+    c, sl = _case(s, [0])
+    try:
+        for mode in (kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE):
+            _, err = _full_check(c, sl, 0, mode, kv.KVOFF_ENGINE_ZEROCOPY)
+            H.log(f"  mode {mode} attention err {err}")
+    finally:
+        H.destroy(c)
+
+
 def test_degenerate_sizes():
     """k >= nb (take every block), k = 1, one-token and one-block contexts."""
     H.log("[degenerate]")
