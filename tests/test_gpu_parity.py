@@ -158,7 +158,7 @@ def test_group_consensus_rule(lam, engine):
         H.destroy(c)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 2), (16, 16), (64, 4)])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 1), (32, 2), (16, 16), (64, 4), (12, 3), (40, 5)])
 def test_group_sizes(Hq, Hkv):
     H.log(f"[groups] Hq {Hq} Hkv {Hkv}")
     s = synth.spec(2, B=2, Hq=Hq, Hkv=Hkv, ctx=2000, k=12, hot=5, headwise=Hkv > 1)
