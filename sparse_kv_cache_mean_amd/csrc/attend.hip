@@ -41,6 +41,7 @@ namespace {
 constexpr int ATT_WAVES = 4;
 constexpr int PART = 2 + kHeadDim;  // m, l, o[128]
 
+
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -189,125 +190,133 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
 
-#pragma unroll 1
-  for (int k = 0; k < 4; ++k) {
-    if (i0 + k >= i1) break;
-    const int blk = blk_w[k];
-    const int64_t ent = ent_w[k];
-    const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
-    const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
+  // K tile as MFMA A operands / VALU dot operands, V rows for the PV product
+  auto load_tiles = [&](const uint16_t* Kp, uint4 (&kf)[TILES][4], uint4 (&vf)[BS / 4]) {
     const uint16_t* Vp = Kp + BS * D;
-    const int n_valid = (int)min<int64_t>(BS, (int64_t)rq.n_tokens - (int64_t)blk * BS);
-    if (ent < 0 || blk < 0 || n_valid <= 0) continue;  // not a valid entry: nothing to read
-
-    uint4 kf[TILES][4];
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         kf[t][m] = load16(Kp + (t * 16 + col) * D + m * 32 + quad * 8);
-    uint4 vf[BS / 4];
 #pragma unroll
     for (int k = 0; k < BS / 4; ++k) vf[k] = load16(Vp + (quad + 4 * k) * D + col * 8);
-
-    if constexpr (MFMA) {
-      float z[TILES][4];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mfma16x16x32<BF16>(kf[t][m], qf[m], acc);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = t * 16 + quad * 4 + v;
-          z[t][v] = tok < n_valid ? acc[v] * a.scale_log2 : -INFINITY;
-        }
-      }
-      float bm = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) bm = fmaxf(bm, z[t][v]);
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m_run, bm);
-      const float alpha = exp2f(m_run - m_new);
-      float ps = 0.f;
-      wave_sync_lds();
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = exp2f(z[t][v] - m_new);
-          ps += p;
-          if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
-        }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
-      wave_sync_lds();
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float al = alpha_s[wave][h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= al;
-      }
-    } else {
-      // z[t][h]: logit of token t*16 + col for head h, partial over the
-      // lane's 32 dims, then summed across the four quads
-      float z[TILES][GV];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-#pragma unroll
-        for (int h = 0; h < GV; ++h) {
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            acc = dot2<BF16>(kf[t][m].x, qv[h][m].x, acc);
-            acc = dot2<BF16>(kf[t][m].y, qv[h][m].y, acc);
-            acc = dot2<BF16>(kf[t][m].z, qv[h][m].z, acc);
-            acc = dot2<BF16>(kf[t][m].w, qv[h][m].w, acc);
-          }
-          acc += __shfl_xor(acc, 16);
-          acc += __shfl_xor(acc, 32);
-          z[t][h] = t * 16 + col < n_valid ? acc * a.scale_log2 : -INFINITY;
-        }
-      wave_sync_lds();
-#pragma unroll
-      for (int h = 0; h < GV; ++h) {
-        float bm = z[0][h];
-#pragma unroll
-        for (int t = 1; t < TILES; ++t) bm = fmaxf(bm, z[t][h]);
-        bm = row_max<16>(bm);
-        const float m_new = fmaxf(mh[h], bm);
-        const float alpha = exp2f(mh[h] - m_new);
-        float ps = 0.f;
-#pragma unroll
+  };
+  // one block: logits, online softmax update, PV
+  auto process = [&](const uint4 (&kf)[TILES][4], const uint4 (&vf)[BS / 4], int n_valid) {
+      if constexpr (MFMA) {
+        float z[TILES][4];
+  #pragma unroll
         for (int t = 0; t < TILES; ++t) {
-          const float p = exp2f(z[t][h] - m_new);
-          ps += p;
-          if ((h & 3) == quad) p_s[wave][t * 16 + col][h] = p;
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+          for (int m = 0; m < 4; ++m) acc = mfma16x16x32<BF16>(kf[t][m], qf[m], acc);
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int tok = t * 16 + quad * 4 + v;
+            z[t][v] = tok < n_valid ? acc[v] * a.scale_log2 : -INFINITY;
+          }
         }
-        lh[h] = lh[h] * alpha + row_sum<16>(ps);
-        mh[h] = m_new;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+        float bm = -INFINITY;
+  #pragma unroll
+        for (int t = 0; t < TILES; ++t)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) bm = fmaxf(bm, z[t][v]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m_run, bm);
+        const float alpha = exp2f(m_run - m_new);
+        float ps = 0.f;
+        wave_sync_lds();
+  #pragma unroll
+        for (int t = 0; t < TILES; ++t)
+  #pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p = exp2f(z[t][v] - m_new);
+            ps += p;
+            if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
+          }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
+        wave_sync_lds();
+  #pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float al = alpha_s[wave][h];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] *= al;
+        }
+      } else {
+        // z[t][h]: logit of token t*16 + col for head h, partial over the
+        // lane's 32 dims, then summed across the four quads
+        float z[TILES][GV];
+  #pragma unroll
+        for (int t = 0; t < TILES; ++t)
+  #pragma unroll
+          for (int h = 0; h < GV; ++h) {
+            float acc = 0.f;
+  #pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              acc = dot2<BF16>(kf[t][m].x, qv[h][m].x, acc);
+              acc = dot2<BF16>(kf[t][m].y, qv[h][m].y, acc);
+              acc = dot2<BF16>(kf[t][m].z, qv[h][m].z, acc);
+              acc = dot2<BF16>(kf[t][m].w, qv[h][m].w, acc);
+            }
+            acc += __shfl_xor(acc, 16);
+            acc += __shfl_xor(acc, 32);
+            z[t][h] = t * 16 + col < n_valid ? acc * a.scale_log2 : -INFINITY;
+          }
+        wave_sync_lds();
+  #pragma unroll
+        for (int h = 0; h < GV; ++h) {
+          float bm = z[0][h];
+  #pragma unroll
+          for (int t = 1; t < TILES; ++t) bm = fmaxf(bm, z[t][h]);
+          bm = row_max<16>(bm);
+          const float m_new = fmaxf(mh[h], bm);
+          const float alpha = exp2f(mh[h] - m_new);
+          float ps = 0.f;
+  #pragma unroll
+          for (int t = 0; t < TILES; ++t) {
+            const float p = exp2f(z[t][h] - m_new);
+            ps += p;
+            if ((h & 3) == quad) p_s[wave][t * 16 + col][h] = p;
+          }
+          lh[h] = lh[h] * alpha + row_sum<16>(ps);
+          mh[h] = m_new;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+        }
+        wave_sync_lds();
       }
-      wave_sync_lds();
-    }
-#pragma unroll
-    for (int k = 0; k < BS / 4; ++k) {
-      float vv[8];
-      unpack8<BF16>(vf[k], vv);
-      const int t = quad + 4 * k;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = p_s[wave][t][h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+  #pragma unroll
+      for (int k = 0; k < BS / 4; ++k) {
+        float vv[8];
+        unpack8<BF16>(vf[k], vv);
+        const int t = quad + 4 * k;
+  #pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = p_s[wave][t][h];
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+        }
       }
+  };
+
+  {
+#pragma unroll 1
+    for (int k = 0; k < 4; ++k) {
+      if (i0 + k >= i1) break;
+      const int blk = blk_w[k];
+      const int64_t ent = ent_w[k];
+      const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
+      const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
+      const int n_valid = (int)min<int64_t>(BS, (int64_t)rq.n_tokens - (int64_t)blk * BS);
+      if (ent < 0 || blk < 0 || n_valid <= 0) continue;  // not a valid entry: nothing to read
+      uint4 kf[TILES][4], vf[BS / 4];
+      load_tiles(Kp, kf, vf);
+      process(kf, vf, n_valid);
     }
   }
 
