@@ -152,6 +152,23 @@ def hbm_copy_peak():
     return best
 
 
+def d2h_link_peak():
+    """Device -> pinned host: best of 5 one-GiB hipMemcpyAsync copies."""
+    nbytes = 1 << 30
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    for _ in range(5):
+        s.record()
+        host.copy_(dev, non_blocking=True)
+        e.record()
+        e.synchronize()
+        best = max(best, nbytes / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del host, dev
+    return best
+
+
 def offload_timing(case, sp, inputs, B):
     """Setup row, outside the step: kvoff_offload_blocks for layer 0 of every
     request again (same bytes, same digests), K and V already in HBM, timed
@@ -171,8 +188,11 @@ def offload_timing(case, sp, inputs, B):
     ms = e0.elapsed_time(e1)
     rec = kv.kvoff_record_bytes(case.ctx) * sum(rq.nb for rq in case.reqs)
     del kd, vd
+    gbps = rec / (ms * 1e-3) / 1e9
+    peak = d2h_link_peak()
     return {"what": f"kvoff_offload_blocks, one layer of {B} requests", "ms_per_layer": round(ms, 3),
-            "host_write_bytes": rec, "host_write_gbps": round(rec / (ms * 1e-3) / 1e9, 2)}
+            "host_write_bytes": rec, "host_write_gbps": round(gbps, 2),
+            "d2h_link_peak_gbps": round(peak, 2), "frac_of_d2h_link_peak": round(gbps / peak, 4)}
 
 
 def cpu_baseline(sp, inputs, B, budget_s):
