@@ -13,7 +13,8 @@
 // score_kernel: HBM-bound streaming of the fp32 digests.  Each wave handles
 // SCORE_BPW consecutive blocks of one request; a lane loads 16 bytes per
 // 1 KiB chunk of a block's [Hkv][d] digest row (coalesced dwordx4 loads), does
-// fp64 FMAs against its slice of u, and the wave reduces with lane shuffles.
+// fp64 FMAs against its slice of u, and the wave reduces with DPP lane moves
+// inside rows of 16 lanes and shuffles across rows.
 //
 // Consensus modes: across KV heads (KVOFF_CONSENSUS) the per-KV-head sums
 // are combined into one shared score; within a GQA group
@@ -60,6 +61,28 @@ struct ScoreArgs {
 };
 
 enum { MODE_SOLO = 0, MODE_HEADWISE = 1, MODE_CONSENSUS = 2, MODE_GROUP = 3 };
+
+// fp64 lane moves within a row of 16 lanes (DPP: no trip through the LDS
+// crossbar that a shuffle takes)
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double x) {
+  const int lo = __double2loint(x), hi = __double2hiint(x);
+  return __hiloint2double(__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false),
+                          __builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 32 lanes, the result in every lane of the
+// group: xor 1 and xor 2 inside quads, then the mirrored half of each 8 and
+// each 16 lanes (by then every lane of a quad / of 8 lanes holds the same
+// partial), then one shuffle across the two rows.  Additions commute, so
+// every lane ends with the same bits.
+__device__ __forceinline__ double sum32(double v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x140>(v);  // row_mirror
+  return v + __shfl_xor(v, 16);
+}
 
 template <bool BF16>
 __device__ __forceinline__ double widen_t(uint16_t h) {
@@ -166,8 +189,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
             acc = fma(widen_t<BF16>((uint16_t)(w.y & 0xffffu)), (double)v[k][c].z, acc);
             acc = fma(widen_t<BF16>((uint16_t)(w.y >> 16)), (double)v[k][c].w, acc);
           }
-#pragma unroll
-          for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+          acc = sum32(acc);
           mx[c] = fmax(mx[c], acc);
           sm[c] += acc;
         }
@@ -200,8 +222,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         acc = fma(u[c][2], (double)v[k][c].z, acc);
         acc = fma(u[c][3], (double)v[k][c].w, acc);
       }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+      acc = sum32(acc);
+      acc += __shfl_xor(acc, 32);
       if (lane == 0 && b < rq.nb) a.scores[(int64_t)r * a.stride + b] = acc;
     } else {
       // per-KV-head sums: a KV head's 128 dims are 32 consecutive lanes of
@@ -214,9 +236,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         acc = fma(u[c][1], (double)v[k][c].y, acc);
         acc = fma(u[c][2], (double)v[k][c].z, acc);
         acc = fma(u[c][3], (double)v[k][c].w, acc);
-#pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        sg[c] = acc;
+        sg[c] = sum32(acc);
       }
       if constexpr (MODE == MODE_HEADWISE) {
 #pragma unroll
