@@ -15,6 +15,7 @@ Prints one JSON line.  `--gpus N` with N > 1 exits: the benchmark measures one G
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import math
 import os
@@ -195,6 +196,33 @@ def offload_timing(case, sp, inputs, B):
             "d2h_link_peak_gbps": round(peak, 2), "frac_of_d2h_link_peak": round(gbps / peak, 4)}
 
 
+def host_cpu():
+    """The host the baseline ran on: CPU model string, the CPUs this process
+    may run on, and the NUMA nodes those CPUs belong to."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    allowed = sorted(os.sched_getaffinity(0))
+    nodes = []
+    for path in sorted(glob.glob("/sys/devices/system/node/node[0-9]*/cpulist")):
+        cpus = set()
+        with open(path) as f:
+            for part in f.read().strip().split(","):
+                if part:
+                    a, _, b = part.partition("-")
+                    cpus.update(range(int(a), int(b or a) + 1))
+        if cpus.intersection(allowed):
+            nodes.append(int(os.path.basename(os.path.dirname(path))[4:]))
+    return {"cpu": model, "nproc": os.cpu_count(), "cpus_allowed": len(allowed),
+            "numa_nodes": nodes}
+
+
 def cpu_baseline(sp, inputs, B, budget_s):
     """The oracle, as it is, on host cores: one request's layer-step (score,
     select, record gather of the selected blocks, fp32 attention) per call.
@@ -242,7 +270,7 @@ def cpu_baseline(sp, inputs, B, budget_s):
                       f"scaled to a {B}-request layer-step",
             "single_thread": {"value": single, "cores": 1,
                               "sample": f"{done} request-steps ({el1:.1f} s)"},
-            "cpu": platform.processor() or platform.machine(), "nproc": os.cpu_count()}
+            **host_cpu()}
 
 
 def fragmentation_report(args):
