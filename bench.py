@@ -81,13 +81,16 @@ def parse():
     p.add_argument("--no-overlap", action="store_true",
                    help="time the serial order on one stream as the value instead of "
                         "kvoff_step (every gather then runs alone: clean kernel traces)")
-    p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass", "decode32"], default=None,
+    p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass", "decode32",
+                                        "attention-cache"], default=None,
                    help="instead of the bench line: fragmentation = recall of the "
                         "headwise-vs-SoloHead workload with every engine; admission = the "
                         "admission policy as a control loop over the multi-layer step; groups = "
                         "interruptible per-request scheduling on the variable-recall layer; "
                         "mass = attention mass kept and recall volume of every selection mode; "
-                        "decode32 = the overlapped 32-layer decode step")
+                        "decode32 = the overlapped 32-layer decode step; attention-cache = "
+                        "sparse attention with its input warm, after a 1 GiB read and after "
+                        "a 1 GiB write")
     return p.parse_args()
 
 
@@ -539,6 +542,64 @@ def mass_report(args):
     print(json.dumps(res), flush=True)
 
 
+def attention_cache_report(args):
+    """Sparse attention on the Llama-3-8B-shaped and the variable-recall
+    layers, three ways: warm (calls back to back; 128 MiB of records stay in
+    the 256 MB MALL, 923 MiB do not), after a 1 GiB read (the records come
+    from HBM, the caches hold clean lines), and after a 1 GiB write (the
+    caches hold dirty lines that the attention's reads must evict).  Per shape
+    and phase, 20 decode calls (attend_kernel + combine_kernel) in that order,
+    so a kernel trace of this report splits into groups of 20 attend_kernel
+    launches; the figures here are event-timed decode calls, median of the
+    last 15.  Each phase's calls are queued while a spin kernel holds the
+    GPU, so the events time the GPU work, not the host's launch latency."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush.fill_(1)
+    out = []
+    for name in ("llama3-8b-layer", "llama3-70b-variable"):
+        sp = synth.spec(name)
+        reqs = synth.request_draws(sp)
+        log(f"generating '{sp.name}'")
+        case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                            [0], reqs, keep=lambda l, r: False)
+        mode = kv.KVOFF_SOLOHEAD
+        bufs = H.make_buffers(case, mode)
+        topk = [rq.k for rq in reqs]
+        kv.kvoff_select(case.ctx, 0, case.rids, case.q[0], case.digest[0], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+        kv.kvoff_recall(case.ctx, 0, case.rids, mode, bufs.sel_idx, bufs.sel_cnt, case.k_stride,
+                        None, None, 0, case.pool, case.n_slots, case.recall_base[0], bufs.table,
+                        kv.KVOFF_ENGINE_ZEROCOPY)
+        scale = 1.0 / math.sqrt(sp.d)
+        nbytes = sum(min(rq.k, rq.nb) for rq in reqs) * kv.kvoff_record_bytes(case.ctx)
+        res = {"workload": name, "records_read_bytes": nbytes}
+        for phase, before in (("warm", None), ("after_1GiB_read", lambda i: flush.view(torch.float32).sum()),
+                              ("after_1GiB_write", lambda i: flush.fill_(i & 0xff))):
+            evs = []
+            torch.cuda.synchronize()
+            torch.cuda._sleep(20_000_000)  # a few ms: every call below is queued before it ends
+            for i in range(20):
+                if before:
+                    before(i)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[0], case.pool, bufs.table,
+                                       bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale, bufs.out,
+                                       bufs.ws)
+                e1.record()
+                evs.append((e0, e1))
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in evs[5:]]))
+            res[phase] = {"decode_us": round(ms * 1e3, 1), "tbps": round(nbytes / (ms * 1e-3) / 1e12, 2)}
+        log(str(res))
+        out.append(res)
+        H.destroy(case)
+        del case, bufs
+        torch.cuda.empty_cache()
+    print(json.dumps({"what": "kvoff_sparse_decode (attend_kernel + combine_kernel), event-timed, "
+                              "median of 15 calls", "runs": out}), flush=True)
+
+
 def decode32_report(args):
     """The 32-layer decode step (batch 8, context 32768, top-64 per layer,
     about 34 GB of pinned host KV): kvoff_step over all layers with recall of
@@ -629,6 +690,8 @@ def main():
         return mass_report(args)
     if args.report == "decode32":
         return decode32_report(args)
+    if args.report == "attention-cache":
+        return attention_cache_report(args)
     sp = synth.spec(args.config if args.config else args.workload, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)
