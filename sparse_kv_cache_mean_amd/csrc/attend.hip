@@ -16,7 +16,8 @@
 //        contiguous bytes of a row.
 //   QK on the matrix cores (MFMA=true): v_mfma_f32_16x16x32_{bf16,f16} with
 //        A = that 16-token x 32-dim tile and B = the G query heads of the
-//        group (columns >= G are zero).  Lane (quad, col) gets the logits of
+//        group (columns >= G repeat the last head; their logits are never
+//        stored).  Lane (quad, col) gets the logits of
 //        tokens quad*4..quad*4+3 for head col; the running max / sum per head
 //        is reduced across the four quads with lane shuffles.
 //   QK on the vector ALUs (MFMA=false, G <= 8): v_dot2 over the same tile
@@ -153,12 +154,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   uint4 qf[4];
   uint4 qv[GV][4];
   if constexpr (MFMA) {
+    // columns col >= G repeat head G-1: MFMA output columns are independent
+    // and those columns' logits are never stored, so they need no zeroing
     const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + min(col, G - 1)) * D;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      qf[m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
-      if (col >= G) qf[m] = make_uint4(0, 0, 0, 0);
-    }
+    for (int m = 0; m < 4; ++m) qf[m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
   } else {
 #pragma unroll
     for (int h = 0; h < GV; ++h) {
