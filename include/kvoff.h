@@ -96,8 +96,9 @@ enum {
   KVOFF_ENGINE_DMA = 1,
   /* the guide's three-phase engine ("The Gather-Scatter I/O Engine"): host
      worker threads gather the selected records into a pinned staging
-     buffer, which bulk hipMemcpyAsync copies (4 MiB chunks, issued as they
-     fill) move to HBM.  Items are placed compactly: the n-th recalled item
+     buffer, which bulk hipMemcpyAsync copies (chunks of 1 MiB, 3 MiB, then
+     16 MiB each, each issued as soon as it is filled; the stats count these
+     copies as transfers) move to HBM.  Items are placed compactly: the n-th recalled item
      of the call (in request, [KV head,] rank order) goes to slot
      recall_base_slot + n (headwise: slice recall_base_slot*Hkv + n); the
      block table says where.  Synchronises the stream first; the staging

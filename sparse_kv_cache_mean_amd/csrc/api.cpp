@@ -161,6 +161,7 @@ int kvoff_destroy(kvoff_ctx* ctx) {
   if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
   if (ctx->stage_buf) (void)hipHostFree(ctx->stage_buf);
   if (ctx->table_host) (void)hipHostFree(ctx->table_host);
+  if (ctx->sel_host) (void)hipHostFree(ctx->sel_host);
   if (ctx->d_counters) (void)hipFree(ctx->d_counters);
   if (ctx->d_reqs) (void)hipFree(ctx->d_reqs);
   if (ctx->store) (void)hipHostFree(ctx->store);

@@ -63,6 +63,8 @@ struct kvoff_ctx {
   size_t stage_cap = 0;
   void* table_host = nullptr;               // pinned block-table staging
   size_t table_cap = 0;
+  void* sel_host = nullptr;                 // pinned read-back of the selection and pool maps
+  size_t sel_cap = 0;
   hipEvent_t ev_stage = nullptr;            // behind the last staged copy
   std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)

@@ -19,11 +19,14 @@
 #include <emmintrin.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <condition_variable>
-#include <deque>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -32,50 +35,99 @@
 
 namespace kvoff {
 
-constexpr size_t kStageChunk = 4u << 20;
+// steady chunk size (measured over 4, 8, 16 and 32 MiB: 16 MiB is best on the
+// variable-recall layer and level with 8 MiB on the Llama-3-8B layer);
+// KVOFF_STAGE_CHUNK_MIB (4..64) overrides it for tuning
+constexpr size_t kStageChunk = 16u << 20;
 
-// Fixed-size pool of host worker threads running copy tasks.
+size_t stage_chunk() {
+  static const size_t c = [] {
+    const char* e = std::getenv("KVOFF_STAGE_CHUNK_MIB");
+    const long v = e ? std::atol(e) : 0;
+    return v >= 4 && v <= 64 ? (size_t)v << 20 : kStageChunk;
+  }();
+  return c;
+}
+
+// One recall's copy work: n tasks, fn(t) for each, and per chunk of the
+// staging buffer the number of its tasks still to finish.  Owned jointly by
+// the issuing thread and every worker that picked it up, so a worker that
+// arrives after the last task was claimed still finds the counters alive.
+struct StageJob {
+  std::atomic<size_t> next{0};
+  size_t n = 0;
+  std::function<void(size_t)> fn;
+  std::vector<uint32_t> chunk_of;                // task -> chunk
+  std::unique_ptr<std::atomic<int>[]> left;      // chunk -> tasks not yet done
+  void work() {
+    for (;;) {
+      const size_t t = next.fetch_add(1, std::memory_order_relaxed);
+      if (t >= n) return;
+      fn(t);
+      left[chunk_of[t]].fetch_sub(1, std::memory_order_release);
+    }
+  }
+};
+
+// Fixed-size pool of host worker threads.  The issuing thread publishes one
+// job at a time; workers take task indices from its counter.  Between jobs a
+// worker spins for a while before it sleeps: in a decode loop the next
+// layer's recall follows within a few hundred microseconds and then finds it
+// awake, where a sleeping thread costs a wake-up of up to hundreds of
+// microseconds before the link can start.
 class StagePool {
  public:
   explicit StagePool(int n) {
-    for (int i = 0; i < n; ++i) workers_.emplace_back([this] { run(); });
+    for (int i = 0; i < n; ++i) workers_.emplace_back([this] { worker(); });
   }
   ~StagePool() {
     {
       std::lock_guard<std::mutex> g(mu_);
-      stop_ = true;
+      stop_.store(true);
     }
     cv_.notify_all();
     for (auto& t : workers_) t.join();
   }
-  void submit(std::function<void()> f) {
+  void run(std::shared_ptr<StageJob> j) {
     {
       std::lock_guard<std::mutex> g(mu_);
-      q_.push_back(std::move(f));
+      job_ = std::move(j);
+      gen_.fetch_add(1, std::memory_order_release);
     }
-    cv_.notify_one();
+    cv_.notify_all();
   }
   int size() const { return (int)workers_.size(); }
 
  private:
-  void run() {
+  static constexpr std::chrono::microseconds kSpin{500};
+  void worker() {
+    uint64_t seen = 0;
     for (;;) {
-      std::function<void()> f;
-      {
-        std::unique_lock<std::mutex> l(mu_);
-        cv_.wait(l, [this] { return stop_ || !q_.empty(); });
-        if (stop_ && q_.empty()) return;
-        f = std::move(q_.front());
-        q_.pop_front();
+      // wait for a job newer than the last one seen: spin, then sleep
+      const auto t0 = std::chrono::steady_clock::now();
+      while (gen_.load(std::memory_order_acquire) == seen && !stop_.load()) {
+        _mm_pause();
+        if (std::chrono::steady_clock::now() - t0 > kSpin) {
+          std::unique_lock<std::mutex> l(mu_);
+          cv_.wait(l, [&] { return gen_.load() != seen || stop_.load(); });
+        }
       }
-      f();
+      if (stop_.load()) return;
+      std::shared_ptr<StageJob> j;
+      {
+        std::lock_guard<std::mutex> g(mu_);
+        j = job_;
+        seen = gen_.load();
+      }
+      if (j) j->work();
     }
   }
   std::vector<std::thread> workers_;
-  std::deque<std::function<void()>> q_;
+  std::shared_ptr<StageJob> job_;
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<bool> stop_{false};
   std::mutex mu_;
   std::condition_variable cv_;
-  bool stop_ = false;
 };
 
 void stage_pool_destroy(kvoff_ctx* ctx) {
@@ -116,13 +168,6 @@ struct Piece {  // one contiguous source range of the store
   size_t bytes;
 };
 
-// Completion flags of the chunks, waited for in order by the issuing thread.
-struct ChunkDone {
-  std::mutex mu;
-  std::condition_variable cv;
-  std::vector<int> left;  // worker tasks still running, per chunk
-};
-
 int ensure_host(void** buf, size_t* cap, size_t need) {
   if (*cap >= need) return KVOFF_OK;
   if (*buf) KVOFF_HIP(hipHostFree(*buf));
@@ -151,25 +196,30 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
     KVOFF_HIP(hipEventSynchronize(ctx->ev_stage));
     ctx->ev_stage_pending = false;
   }
-  std::vector<int32_t> cnt(b.n), sel(n_sel);
-  std::vector<uint8_t> hit;
-  KVOFF_HIP(hipMemcpyAsync(cnt.data(), r.sel_cnt, sizeof(int32_t) * b.n, hipMemcpyDeviceToHost, stream));
-  KVOFF_HIP(hipMemcpyAsync(sel.data(), r.sel_idx, sizeof(int32_t) * n_sel, hipMemcpyDeviceToHost, stream));
-  if (r.pool_hit) {
-    hit.resize((size_t)b.n * r.pool_stride);
-    KVOFF_HIP(hipMemcpyAsync(hit.data(), r.pool_hit, hit.size(), hipMemcpyDeviceToHost, stream));
-  }
-  std::vector<int32_t> pslot;
-  if (r.pool_slot) {
-    pslot.resize((size_t)b.n * r.pool_stride);
-    KVOFF_HIP(hipMemcpyAsync(pslot.data(), r.pool_slot, pslot.size() * sizeof(int32_t),
-                             hipMemcpyDeviceToHost, stream));
-  }
+  // read the selection (and the pool maps) back into pinned memory
+  const size_t n_map = r.pool_hit || r.pool_slot ? (size_t)b.n * r.pool_stride : 0;
+  const size_t o_sel = ((size_t)b.n * sizeof(int32_t) + 255) & ~(size_t)255;
+  const size_t o_slot = (o_sel + n_sel * sizeof(int32_t) + 255) & ~(size_t)255;
+  const size_t o_hit = (o_slot + (r.pool_slot ? n_map * sizeof(int32_t) : 0) + 255) & ~(size_t)255;
+  int st = ensure_host(&ctx->sel_host, &ctx->sel_cap, o_hit + (r.pool_hit ? n_map : 0) + 1);
+  if (st) return st;
+  uint8_t* rb = (uint8_t*)ctx->sel_host;
+  const int32_t* cnt = (const int32_t*)rb;
+  const int32_t* sel = (const int32_t*)(rb + o_sel);
+  const int32_t* pslot = (const int32_t*)(rb + o_slot);
+  const uint8_t* hit = rb + o_hit;
+  KVOFF_HIP(hipMemcpyAsync(rb, r.sel_cnt, sizeof(int32_t) * b.n, hipMemcpyDeviceToHost, stream));
+  KVOFF_HIP(hipMemcpyAsync(rb + o_sel, r.sel_idx, sizeof(int32_t) * n_sel, hipMemcpyDeviceToHost, stream));
+  if (r.pool_hit)
+    KVOFF_HIP(hipMemcpyAsync(rb + o_hit, r.pool_hit, n_map, hipMemcpyDeviceToHost, stream));
+  if (r.pool_slot)
+    KVOFF_HIP(hipMemcpyAsync(rb + o_slot, r.pool_slot, n_map * sizeof(int32_t), hipMemcpyDeviceToHost,
+                             stream));
   KVOFF_HIP(hipStreamSynchronize(stream));
 
   // plan: compact order of the missing items, their block-table entries and
   // the source pieces (consecutive blocks of one request coalesced)
-  int st = ensure_host(&ctx->table_host, &ctx->table_cap, n_sel * sizeof(int32_t));
+  st = ensure_host(&ctx->table_host, &ctx->table_cap, n_sel * sizeof(int32_t));
   if (st) return st;
   int32_t* table = (int32_t*)ctx->table_host;
   std::vector<Piece> pieces;
@@ -218,49 +268,68 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   }
   if ((st = ensure_host(&ctx->stage_buf, &ctx->stage_cap, total))) return st;
   if (!ctx->stage_pool) {
+    // one hardware thread is left to the issuing thread, which spins on the
+    // chunk counters while the workers copy
     const unsigned hc = std::thread::hardware_concurrency();
-    ctx->stage_pool = new StagePool((int)std::max(1u, std::min(16u, hc ? hc : 4u)));
+    ctx->stage_pool = new StagePool((int)std::max(1u, std::min(15u, (hc ? hc : 4u) - 1)));
   }
 
-  // one worker task per 1 MiB of staging (kStageChunk / 4): it copies every
-  // piece, or part of a piece, that lands in its range.  A chunk's bulk copy
-  // is issued once its four tasks are done.
-  constexpr size_t kTask = kStageChunk / 4;  // measured: 256 KiB to 2 MiB, 1 MiB is best
-  const size_t n_chunks = (total + kStageChunk - 1) / kStageChunk;
-  const size_t n_tasks = (total + kTask - 1) / kTask;
-  ChunkDone done;
-  done.left.assign(n_chunks, 0);
-  for (size_t t = 0; t < n_tasks; ++t) ++done.left[t * kTask / kStageChunk];
+  // Chunks of the staging buffer, each one bulk copy: 1 MiB, then 3 MiB,
+  // then 16 MiB each, so the link starts as soon as the first megabyte is
+  // gathered, and later copies are long enough that the copy engine's
+  // per-copy cost stays small.  Worker tasks: 256 KiB in the first two
+  // chunks, so that every worker helps fill them, then 1 MiB (measured:
+  // smaller tasks throughout cost more in hand-offs than they gain).  A task
+  // copies every piece, or part of a piece, that lands in its range.
+  std::vector<size_t> chunk_lo{0};
+  for (size_t o = 0; o < total;) {
+    const size_t c = chunk_lo.size() - 1;
+    o = std::min(total, o + (c == 0 ? (1u << 20) : c == 1 ? (3u << 20) : stage_chunk()));
+    chunk_lo.push_back(o);
+  }
+  const size_t n_chunks = chunk_lo.size() - 1;
+  auto job = std::make_shared<StageJob>();
+  std::vector<size_t> task_lo;
+  for (size_t c = 0; c < n_chunks; ++c) {
+    const size_t step = c < 2 ? (256u << 10) : (1u << 20);
+    for (size_t o = chunk_lo[c]; o < chunk_lo[c + 1]; o += step) {
+      task_lo.push_back(o);
+      job->chunk_of.push_back((uint32_t)c);
+    }
+  }
+  task_lo.push_back(total);
+  job->n = task_lo.size() - 1;
+  job->left.reset(new std::atomic<int>[n_chunks]);
+  for (size_t c = 0; c < n_chunks; ++c) job->left[c].store(0, std::memory_order_relaxed);
+  for (size_t t = 0; t < job->n; ++t) job->left[job->chunk_of[t]].fetch_add(1, std::memory_order_relaxed);
   std::vector<size_t> piece_off(pieces.size() + 1, 0);
   for (size_t i = 0; i < pieces.size(); ++i) piece_off[i + 1] = piece_off[i] + pieces[i].bytes;
   uint8_t* stage = (uint8_t*)ctx->stage_buf;
   const Piece* pc = pieces.data();
   const size_t* po = piece_off.data();
+  const size_t* tl = task_lo.data();
   const size_t n_pieces = pieces.size();
-  for (size_t t = 0; t < n_tasks; ++t) {
-    ctx->stage_pool->submit([t, total, stage, pc, po, n_pieces, &done] {
-      const size_t lo = t * kTask, hi = std::min(total, lo + kTask);
-      // first piece overlapping [lo, hi)
-      size_t i = std::upper_bound(po, po + n_pieces + 1, lo) - po - 1;
-      for (; i < n_pieces && po[i] < hi; ++i) {
-        const size_t a = std::max(lo, po[i]), b = std::min(hi, po[i + 1]);
-        copy_streaming(stage + a, pc[i].src + (a - po[i]), b - a);
-      }
-      std::lock_guard<std::mutex> g(done.mu);
-      if (--done.left[t * kTask / kStageChunk] == 0) done.cv.notify_all();
-    });
-  }
-  // issue each chunk's copy as soon as it is filled, in order
+  // fn runs only for claimed tasks, all of which finish before this call
+  // returns, so it may refer to this frame's vectors
+  job->fn = [stage, pc, po, tl, n_pieces](size_t t) {
+    const size_t lo = tl[t], hi = tl[t + 1];
+    // first piece overlapping [lo, hi)
+    size_t i = std::upper_bound(po, po + n_pieces + 1, lo) - po - 1;
+    for (; i < n_pieces && po[i] < hi; ++i) {
+      const size_t a = std::max(lo, po[i]), b = std::min(hi, po[i + 1]);
+      copy_streaming(stage + a, pc[i].src + (a - po[i]), b - a);
+    }
+  };
+  ctx->stage_pool->run(job);
+  // issue each chunk's copy as soon as it is filled, in order; every chunk
+  // is waited for, also after an error, so no task outlives this call
   uint8_t* dst0 = r.pool + (size_t)r.recall_base_slot * ctx->rec_bytes;
   int64_t n_transfers = 0;
   int err = KVOFF_OK;
   for (size_t c = 0; c < n_chunks; ++c) {
-    {
-      std::unique_lock<std::mutex> l(done.mu);
-      done.cv.wait(l, [&] { return done.left[c] == 0; });
-    }
-    const size_t o = c * kStageChunk;
-    const size_t n = std::min(kStageChunk, total - o);
+    while (job->left[c].load(std::memory_order_acquire) != 0) _mm_pause();
+    const size_t o = chunk_lo[c];
+    const size_t n = chunk_lo[c + 1] - o;
     if (err == KVOFF_OK) {
       hipError_t e = hipMemcpyAsync(dst0 + o, stage + o, n, hipMemcpyHostToDevice, stream);
       if (e != hipSuccess) err = fail(KVOFF_EHIP, "staged copy: %s", hipGetErrorString(e));

@@ -91,7 +91,16 @@ def expected_transfers(c, l, mode, slices, with_pool_hits):
     return dict(selected=n_sel, pool_hits=n_hits, items_recalled=n_items, transfers=n_tr)
 
 
-STAGE_CHUNK = 4 << 20  # bulk copy size of the staged engine
+def staged_copies(total_bytes: int) -> int:
+    """Bulk copies the staged engine issues for total_bytes of staging: one
+    of 1 MiB, one of 3 MiB, then one per 16 MiB (the last one partial)."""
+    if total_bytes <= 0:
+        return 0
+    if total_bytes <= 1 << 20:
+        return 1
+    if total_bytes <= 4 << 20:
+        return 2
+    return 2 + -(-(total_bytes - (4 << 20)) // (16 << 20))
 
 
 def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats=None,
@@ -137,7 +146,7 @@ def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats
         exp = expected_transfers(c, l, mode, slices, with_pool_hits)
         item = slice_b if per_head(mode) else rec
         if compact:  # bulk copies of the staging buffer
-            exp["transfers"] = -(-exp["items_recalled"] * item // STAGE_CHUNK)
+            exp["transfers"] = staged_copies(exp["items_recalled"] * item)
         for k, v in exp.items():
             assert stats[k] == v, (k, stats[k], v)
         assert stats["bytes"] == exp["items_recalled"] * item

@@ -376,7 +376,7 @@ def test_step_overlap_matches_serial_and_oracle(engine):
         exp = [P.expected_transfers(c, l, mode, sl, False) for l in layers]
         rec = kv.kvoff_record_bytes(c.ctx)
         if engine == kv.KVOFF_ENGINE_STAGED:  # transfers are the bulk staging copies
-            want_tr = sum(-(-e["items_recalled"] * rec // P.STAGE_CHUNK) for e in exp)
+            want_tr = sum(P.staged_copies(e["items_recalled"] * rec) for e in exp)
         else:
             want_tr = sum(e["transfers"] for e in exp)
         assert stats["transfers"] == want_tr
