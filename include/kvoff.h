@@ -96,14 +96,16 @@ enum {
   KVOFF_ENGINE_DMA = 1,
   /* the guide's three-phase engine ("The Gather-Scatter I/O Engine"): host
      worker threads gather the selected records into a pinned staging
-     buffer, which bulk hipMemcpyAsync copies (chunks of 1 MiB, 3 MiB, then
-     16 MiB each, each issued as soon as it is filled; the stats count these
-     copies as transfers) move to HBM.  Items are placed compactly: the n-th recalled item
-     of the call (in request, [KV head,] rank order) goes to slot
-     recall_base_slot + n (headwise: slice recall_base_slot*Hkv + n); the
-     block table says where.  Synchronises the stream first; the staging
-     buffer (pinned, grown on demand) is reused once the previous call's
-     copies completed. */
+     buffer, which bulk hipMemcpyAsync copies move to HBM: chunks of 1 MiB,
+     3 MiB, then 16 MiB each, each issued as soon as it is filled (the stats
+     count these copies as transfers).  Items are placed compactly: the n-th
+     recalled item of the call (in request, [KV head,] rank order) goes to
+     slot recall_base_slot + n (headwise: slice recall_base_slot*Hkv + n);
+     the block table says where.  Synchronises the stream first and returns
+     once every chunk is gathered and its copy enqueued; the staging buffer
+     (pinned, grown on demand) is reused once the previous call's copies
+     completed.  The context's worker threads (one fewer than the hardware
+     threads, at most 15) spin for 500 us after a call before they sleep. */
   KVOFF_ENGINE_STAGED = 2
 };
 

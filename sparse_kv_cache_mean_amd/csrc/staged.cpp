@@ -5,9 +5,9 @@
 // then bulk host->HBM copies move it across the link.
 //
 // Differences from the guide's description, and why:
-//  - the bulk copy is cut into 4 MiB chunks issued as soon as the workers
-//    have filled them, so gathering and the link transfer overlap instead of
-//    running back to back;
+//  - the bulk copy is cut into chunks (1 MiB, 3 MiB, then 16 MiB) issued
+//    as soon as the workers have filled them, so gathering and the link
+//    transfer overlap instead of running back to back;
 //  - there is no scatter kernel: items are placed compactly, in selection
 //    order, at the start of the recall region and the block table points at
 //    them (item n of the call -> slot recall_base + n; headwise: slice
