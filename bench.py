@@ -91,7 +91,17 @@ def parse():
                         "decode32 = the overlapped 32-layer decode step; attention-cache = "
                         "sparse attention with its input warm, after a 1 GiB read and after "
                         "a 1 GiB write")
-    return p.parse_args()
+    args = p.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        p.error("--steps must be at least 1 and --warmup at least 0")
+    return args
+
+
+def step_calls(n: int, per_call: int) -> list[int]:
+    """Layers per kvoff_step call for exactly n layer-steps: whole passes of
+    per_call layers, then one shorter call over the first n mod per_call."""
+    full, rem = divmod(n, per_call)
+    return [per_call] * full + ([rem] if rem else [])
 
 
 def link_peaks(case):
@@ -604,8 +614,8 @@ def decode32_report(args):
     """The 32-layer decode step (batch 8, context 32768, top-64 per layer,
     about 34 GB of pinned host KV): kvoff_step over all layers with recall of
     layer l+1 on a copy stream under select/attention of layer l, against the
-    same step on one stream.  Warm: each figure is the mean of several steps
-    after one untimed step."""
+    same step on one stream.  Warm: each figure is the mean of 10 steps after
+    one untimed step."""
     sp = synth.spec(3)
     reqs = synth.request_draws(sp)
     B, L = len(reqs), sp.L
@@ -633,7 +643,7 @@ def decode32_report(args):
             ws=sets[0].ws, compute_stream=compute, copy_stream=copy_stream,
             want_stats=want_stats, want_timing=timing, group_requests=grp)
 
-    def timed(copy_stream, n=5, grp=0):
+    def timed(copy_stream, n=10, grp=0):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         first = time.perf_counter()
         step(copy_stream, grp=grp)
@@ -757,14 +767,14 @@ def main():
 
     # 2) the headline: kvoff_step over the rotating layers, recall of layer
     #    l+1 on the copy streams under select/attention of layer l; one call
-    #    is len(layers) layer-steps
+    #    is up to len(layers) layer-steps
     sets = [bufs, H.make_buffers(case, mode)]
     outs = [torch.empty_like(bufs.out) for _ in layers]
     copy = torch.cuda.Stream()
 
-    def step_all(timing=False):
+    def step_all(timing=False, n_layers=None):
         return kv.kvoff_step(
-            case.ctx, layer_begin=0, layer_end=len(layers), req_ids=case.rids,
+            case.ctx, layer_begin=0, layer_end=n_layers or len(layers), req_ids=case.rids,
             topk=topk, mode=mode, engine=engine, k_stride=case.k_stride,
             q=[case.q[l] for l in layers], digest=[case.digest[l] for l in layers],
             digest_stride=case.nb_max, slot_pool=case.pool, n_slots=case.n_slots,
@@ -773,19 +783,20 @@ def main():
             block_table=[b.table for b in sets], scale=scale, out=outs, ws=bufs.ws,
             compute_stream=stream, copy_stream=copy, want_timing=timing)
 
+    def run_steps(n):
+        for n_layers in step_calls(n, len(layers)):
+            step_all(n_layers=n_layers)
+
+    steps_timed, warm_timed = args.steps, args.warmup
     if args.no_overlap:
-        steps_timed, warm_timed, ms_per_step = args.steps, args.warmup, serial_ms
+        ms_per_step = serial_ms
     else:
-        n_calls = -(-args.steps // len(layers))
-        n_warm = -(-args.warmup // len(layers))
-        steps_timed, warm_timed = n_calls * len(layers), n_warm * len(layers)
-        for _ in range(n_warm):
-            step_all()
+        n_calls = max(1, args.steps // len(layers))
+        run_steps(args.warmup)
         torch.cuda.synchronize()
         log(f"timing {steps_timed} layer-steps through kvoff_step")
         t_o = time.perf_counter()
-        for _ in range(n_calls):
-            step_all()
+        run_steps(args.steps)
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t_o) * 1e3 / steps_timed
         # the recall's duration per launch inside this schedule: the same

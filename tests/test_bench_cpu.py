@@ -28,3 +28,19 @@ def test_cpu_baseline_leg_runs_single_and_threaded():
     assert res["value"] > 0 and res["single_thread"]["value"] > 0
     assert 1 <= res["cores"] <= 16
     assert res["single_thread"]["cores"] == 1
+
+
+def test_bench_times_exactly_the_steps_asked_for():
+    """The overlapped headline is timed over kvoff_step calls of up to one
+    pass over the rotating layers; the calls add up to exactly --steps."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for n in range(0, 23):
+        for per in (1, 3, 4):
+            calls = bench.step_calls(n, per)
+            assert sum(calls) == n
+            assert all(1 <= c <= per for c in calls)
+            assert calls[:-1] == [per] * (len(calls) - 1) if calls else True
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "--steps" in r.stderr
