@@ -2,6 +2,8 @@
 // the library's translation units.  Not part of the ABI.
 #pragma once
 
+#include <exception>
+#include <new>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -77,6 +79,22 @@ namespace kvoff {
 // thread-local message of the last failure
 void set_error(const char* fmt, ...);
 int fail(int status, const char* fmt, ...);
+
+// Runs an entry point's body and turns any C++ exception (a failed host
+// allocation, a worker thread that cannot be created) into a status code, so
+// none crosses the C ABI.
+template <class F>
+int guarded(F&& body) noexcept {
+  try {
+    return body();
+  } catch (const std::bad_alloc&) {
+    return fail(KVOFF_ENOMEM, "host memory allocation failed");
+  } catch (const std::exception& e) {
+    return fail(KVOFF_ESTATE, "internal error: %s", e.what());
+  } catch (...) {
+    return fail(KVOFF_ESTATE, "internal error");
+  }
+}
 
 #define KVOFF_HIP(call)                                                            \
   do {                                                                             \

@@ -77,17 +77,16 @@ struct StageJob {
 // microseconds before the link can start.
 class StagePool {
  public:
+  // throws if a thread cannot be started, after stopping the ones that did
   explicit StagePool(int n) {
-    for (int i = 0; i < n; ++i) workers_.emplace_back([this] { worker(); });
-  }
-  ~StagePool() {
-    {
-      std::lock_guard<std::mutex> g(mu_);
-      stop_.store(true);
+    try {
+      for (int i = 0; i < n; ++i) workers_.emplace_back([this] { worker(); });
+    } catch (...) {
+      shutdown();
+      throw;
     }
-    cv_.notify_all();
-    for (auto& t : workers_) t.join();
   }
+  ~StagePool() { shutdown(); }
   void run(std::shared_ptr<StageJob> j) {
     {
       std::lock_guard<std::mutex> g(mu_);
@@ -100,6 +99,15 @@ class StagePool {
 
  private:
   static constexpr std::chrono::microseconds kSpin{500};
+  void shutdown() {
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      stop_.store(true);
+    }
+    cv_.notify_all();
+    for (auto& t : workers_) t.join();
+    workers_.clear();
+  }
   void worker() {
     uint64_t seen = 0;
     for (;;) {
@@ -254,8 +262,8 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
     }
   }
   const size_t total = (size_t)n_items * item;
-  KVOFF_HIP(hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream));
   if (total == 0) {
+    KVOFF_HIP(hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream));
     // the upload reads the block-table staging: the next call (possibly on
     // another stream) waits for this event before rewriting it
     KVOFF_HIP(hipEventRecord(ctx->ev_stage, stream));
@@ -265,13 +273,6 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
       *stats = kvoff_stats{n_selected, n_hits, 0, 0, 0};
     }
     return KVOFF_OK;
-  }
-  if ((st = ensure_host(&ctx->stage_buf, &ctx->stage_cap, total))) return st;
-  if (!ctx->stage_pool) {
-    // one hardware thread is left to the issuing thread, which spins on the
-    // chunk counters while the workers copy
-    const unsigned hc = std::thread::hardware_concurrency();
-    ctx->stage_pool = new StagePool((int)std::max(1u, std::min(15u, (hc ? hc : 4u) - 1)));
   }
 
   // Chunks of the staging buffer, each one bulk copy: 1 MiB, then 3 MiB,
@@ -304,6 +305,16 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   for (size_t t = 0; t < job->n; ++t) job->left[job->chunk_of[t]].fetch_add(1, std::memory_order_relaxed);
   std::vector<size_t> piece_off(pieces.size() + 1, 0);
   for (size_t i = 0; i < pieces.size(); ++i) piece_off[i + 1] = piece_off[i] + pieces[i].bytes;
+  // Everything this call allocates is allocated before the first copy is
+  // enqueued, so a failure leaves no copy in flight that reads the staging
+  // the next call rewrites.
+  if ((st = ensure_host(&ctx->stage_buf, &ctx->stage_cap, total))) return st;
+  if (!ctx->stage_pool) {
+    // one hardware thread is left to the issuing thread, which spins on the
+    // chunk counters while the workers copy
+    const unsigned hc = std::thread::hardware_concurrency();
+    ctx->stage_pool = new StagePool((int)std::max(1u, std::min(15u, (hc ? hc : 4u) - 1)));
+  }
   uint8_t* stage = (uint8_t*)ctx->stage_buf;
   const Piece* pc = pieces.data();
   const size_t* po = piece_off.data();
@@ -320,6 +331,7 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
       copy_streaming(stage + a, pc[i].src + (a - po[i]), b - a);
     }
   };
+  KVOFF_HIP(hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream));
   ctx->stage_pool->run(job);
   // issue each chunk's copy as soon as it is filled, in order; every chunk
   // is waited for, also after an error, so no task outlives this call
