@@ -53,7 +53,11 @@
 extern "C" {
 #endif
 
-/* ---------------------------------------------------------------- status */
+/* ---------------------------------------------------------------- status
+   Every call that returns int returns one of these; the detail of the last
+   failure on the calling thread is in kvoff_last_error().  No C++ exception
+   leaves the library: a failed host allocation inside a call is reported as
+   KVOFF_ENOMEM, any other internal failure as KVOFF_ESTATE. */
 enum {
   KVOFF_OK = 0,
   KVOFF_EINVAL = -1, /* invalid argument or shape                          */
