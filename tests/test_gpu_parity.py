@@ -706,3 +706,61 @@ def test_recall_before_offload_is_rejected():
         assert e.value.status == kv.KVOFF_ESTATE
     finally:
         kv.kvoff_destroy(ctx)
+
+
+@pytest.mark.parametrize("mode", [kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE])
+def test_staged_recall_back_to_back_calls(mode):
+    """Many staged recalls in a row, alternating between two streams, two
+    layers and batches of one to four requests (3 to 4 bulk copies each),
+    every one checked byte for byte and for compact placement: the worker
+    pool hands each call's job over without mixing calls, and the staging
+    buffers are reused only after the previous call's copies."""
+    # 256 blocks, top-64: 8 MiB per request (per-head sets generated too)
+    s = synth.spec(2, B=4, L=2, ctx=8192, headwise=True)
+    H.log(f"[staged back to back] mode {mode}")
+    c, sl = _case(s, [0, 1])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    subsets = [[0, 1, 2, 3], [2], [1, 3], [0], [3, 2, 1, 0], [0, 2, 3], [1]]
+    rec = kv.kvoff_record_bytes(c.ctx)
+    hw = P.per_head(mode)
+    item = rec // s.Hkv if hw else rec
+    base = c.recall_base[0]
+    try:
+        for call in range(14):
+            sub = subsets[call % len(subsets)]
+            l = call % 2
+            st = streams[call % 2]
+            rids = [c.rids[r] for r in sub]
+            idx = torch.tensor(sub, device="cuda")
+            q = c.q[l].index_select(0, idx).contiguous()
+            dg = c.digest[l].index_select(0, idx).contiguous()
+            sets = s.Hkv if hw else 1
+            scores = torch.empty((len(sub), sets, c.nb_max), dtype=torch.float64, device="cuda")
+            sel = torch.empty((len(sub), sets, c.k_stride), dtype=torch.int32, device="cuda")
+            cnt = torch.empty((len(sub),), dtype=torch.int32, device="cuda")
+            table = torch.empty((len(sub), sets, c.k_stride), dtype=torch.int32, device="cuda")
+            topk = [c.reqs[r].k for r in sub]
+            kv.kvoff_select(c.ctx, l, rids, q, dg, c.nb_max, topk, mode, scores, sel, cnt,
+                            c.k_stride, stream=st)
+            stats = kv.kvoff_recall(c.ctx, l, rids, mode, sel, cnt, c.k_stride, None, None, 0,
+                                    c.pool, c.n_slots, base, table, kv.KVOFF_ENGINE_STAGED,
+                                    want_stats=True, stream=st)
+            torch.cuda.synchronize()
+            tab = table.cpu().numpy()
+            pool = c.pool.cpu().numpy()
+            n = 0
+            for i, r in enumerate(sub):
+                for g, bset in enumerate(P.block_sets(sl[(l, r)], mode)):
+                    want = workloads.block_records(sl[(l, r)], bset.tolist())
+                    for j in range(len(bset)):
+                        ent = int(tab[i, g, j])
+                        assert ent == (base * s.Hkv if hw else base) + n, (call, r, g, j, ent)
+                        n += 1
+                        got = pool[ent * item:(ent + 1) * item]
+                        exp = (want[j, g] if hw else want[j]).reshape(-1).view(np.uint8)
+                        assert np.array_equal(got, exp), (call, r, g, j)
+            assert stats["items_recalled"] == n and stats["bytes"] == n * item
+            assert stats["transfers"] == P.staged_copies(n * item), (call, stats)
+        H.log(f"  {call + 1} calls checked")
+    finally:
+        H.destroy(c)
