@@ -82,7 +82,7 @@ def parse():
                    help="time the serial order on one stream as the value instead of "
                         "kvoff_step (every gather then runs alone: clean kernel traces)")
     p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass", "decode32",
-                                        "attention-cache"], default=None,
+                                        "attention-cache", "attention-heads"], default=None,
                    help="instead of the bench line: fragmentation = recall of the "
                         "headwise-vs-SoloHead workload with every engine; admission = the "
                         "admission policy as a control loop over the multi-layer step; groups = "
@@ -90,7 +90,8 @@ def parse():
                         "mass = attention mass kept and recall volume of every selection mode; "
                         "decode32 = the overlapped 32-layer decode step; attention-cache = "
                         "sparse attention with its input warm, after a 1 GiB read and after "
-                        "a 1 GiB write")
+                        "a 1 GiB write; attention-heads = sparse attention with 4, 8 and 16 "
+                        "query heads per KV head over the same records")
     args = p.parse_args()
     if args.steps < 1 or args.warmup < 0:
         p.error("--steps must be at least 1 and --warmup at least 0")
@@ -610,6 +611,53 @@ def attention_cache_report(args):
                               "median of 15 calls", "runs": out}), flush=True)
 
 
+def attention_heads_report(args):
+    """Sparse attention on the Llama-3-8B layer's records (batch 16, 8 KV
+    heads, context 32768, top-64, 128 MiB) with 32, 64 and 128 query heads,
+    i.e. G = 4, 8 and 16 query heads per KV head: the same bytes, G times the
+    arithmetic.  Per G, 20 decode calls queued behind a spin kernel, warm;
+    event-timed, median of the last 15 (a kernel trace of this report splits
+    by attend_kernel's first template argument, G)."""
+    out = []
+    for hq in (32, 64, 128):
+        sp = synth.spec("llama3-8b-layer", Hq=hq)
+        reqs = synth.request_draws(sp)
+        log(f"generating '{sp.name}' with {hq} query heads")
+        case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                            [0], reqs, keep=lambda l, r: False)
+        mode = kv.KVOFF_SOLOHEAD
+        bufs = H.make_buffers(case, mode)
+        topk = [rq.k for rq in reqs]
+        kv.kvoff_select(case.ctx, 0, case.rids, case.q[0], case.digest[0], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+        kv.kvoff_recall(case.ctx, 0, case.rids, mode, bufs.sel_idx, bufs.sel_cnt, case.k_stride,
+                        None, None, 0, case.pool, case.n_slots, case.recall_base[0], bufs.table,
+                        kv.KVOFF_ENGINE_ZEROCOPY)
+        scale = 1.0 / math.sqrt(sp.d)
+        nbytes = sum(min(rq.k, rq.nb) for rq in reqs) * kv.kvoff_record_bytes(case.ctx)
+        evs = []
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)  # a few ms: every call below is queued before it ends
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[0], case.pool, bufs.table,
+                                   bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale, bufs.out, bufs.ws)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs[5:]]))
+        res = {"q_heads": hq, "kv_heads": sp.Hkv, "G": hq // sp.Hkv, "records_read_bytes": nbytes,
+               "decode_us": round(ms * 1e3, 1), "tbps": round(nbytes / (ms * 1e-3) / 1e12, 2)}
+        log(str(res))
+        out.append(res)
+        H.destroy(case)
+        del case, bufs
+        torch.cuda.empty_cache()
+    print(json.dumps({"what": "kvoff_sparse_decode (attend_kernel + combine_kernel), warm, "
+                              "event-timed, median of 15 calls", "runs": out}), flush=True)
+
+
 def decode32_report(args):
     """The 32-layer decode step (batch 8, context 32768, top-64 per layer,
     about 34 GB of pinned host KV): kvoff_step over all layers with recall of
@@ -702,6 +750,8 @@ def main():
         return decode32_report(args)
     if args.report == "attention-cache":
         return attention_cache_report(args)
+    if args.report == "attention-heads":
+        return attention_heads_report(args)
     sp = synth.spec(args.config if args.config else args.workload, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)

@@ -24,9 +24,20 @@
 //        against the lane's 32 query dims of every head, summed across the
 //        four quads; every lane then holds all G heads' logits of its two
 //        tokens and the per-head max / sum are reduced across the 16 columns.
-//   softmax  log2 domain; probabilities go to LDS.
-//   PV   fp32 VALU: lane (token group quad, dim group col) loads 16 bytes of
-//        V rows t = quad + 4k and accumulates o[h][8 dims] for all G heads.
+//   softmax  log2 domain.
+//   PV, G <= 4 (or 16-token blocks): fp32 VALU.  Probabilities go to LDS;
+//        lane (token group quad, dim group col) loads 16 bytes of V rows
+//        t = quad + 4k and accumulates o[h][8 dims] for all G heads.
+//   PV, G >= 8 with MFMA QK and 32-token blocks: on the matrix cores.  The
+//        K rows of the QK tiles are loaded in an order that leaves quad q
+//        with the logits of the consecutive tokens 8q .. 8q+7, so each lane
+//        already holds its row of the A operand P (heads x 32 tokens), split
+//        into hi and lo halves of the storage type (fp16: scaled by 2^15).
+//        V goes through LDS (rows padded to 132 elements, so the column
+//        reads of the four quads fall in different banks) and each lane
+//        gathers its B operand column V[8q .. 8q+7][dim]; one MFMA pair per
+//        16-dim chunk accumulates o[head][dim] with no cross-quad sum.  At
+//        G = 4 the VALU form is faster: it keeps 3 waves per SIMD.
 // The four waves merge in LDS; one partial (m, l, o[128]) per (head, split)
 // goes to the workspace and combine_kernel merges the splits in fixed split
 // order, so results are deterministic.  (Merging in the last-arriving
@@ -122,16 +133,32 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <int G, int BS, bool BF16, bool MFMA>
 __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
   static_assert(MFMA || G <= 8, "the VALU QK keeps every head's query slice in registers");
+  static_assert(G <= 16, "one MFMA tile holds the group's heads");
   constexpr int D = kHeadDim;
   constexpr int TILES = BS / 16;
   constexpr int GV = MFMA ? 1 : G;  // heads whose query slice a lane holds (VALU)
-  __shared__ float p_s[ATT_WAVES][BS][G];
-  __shared__ float alpha_s[ATT_WAVES][G];
+  // P V on the matrix cores too (32-token blocks, G >= 8): P (heads x
+  // tokens) from registers as the A operand, V (tokens x dims) through LDS as
+  // B.  Measured at the Llama-3-8B layer's 128 MiB: G = 16 68.9 -> 30.8 us,
+  // G = 8 32.1 -> 28.4 us, G = 4 24.5 -> 27.0 us (its 32 accumulator
+  // registers cost G = 4 a wave per SIMD, and its VALU P V is cheap), so G = 4
+  // and below keep the VALU P V.
+  constexpr bool PVM = MFMA && BS == 32 && G >= 8;
+  constexpr int VS = 132;  // LDS row stride of the V tile (elements): column reads hit 4 bank groups
+  __shared__ float p_s[ATT_WAVES][PVM ? 1 : BS][G];
+  __shared__ float alpha_s[ATT_WAVES][PVM ? 16 : G];
   __shared__ float wm[ATT_WAVES][G], wl[ATT_WAVES][G];
   __shared__ float wo[ATT_WAVES][G][D];
+  __shared__ uint16_t v_s[ATT_WAVES][PVM ? BS * VS : 1];
 
   const int s = blockIdx.x % a.S;
   const int rg = blockIdx.x / a.S;
@@ -184,20 +211,27 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     mh[h] = -INFINITY;
     lh[h] = 0.f;
   }
-  float o[G][8];
+  float o[PVM ? 1 : G][8];  // VALU P V: heads x the lane's 8 dims
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < (PVM ? 1 : G); ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  // MFMA P V: per 16-dim chunk c, heads quad*4 + i at dim c*16 + col
+  f32x4_t oc[PVM ? 8 : 1];
+#pragma unroll
+  for (int c = 0; c < (PVM ? 8 : 1); ++c) oc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // K tile as MFMA A operands / VALU dot operands, V rows for the PV product
   auto load_tiles = [&](const uint16_t* Kp, uint4 (&kf)[TILES][4], uint4 (&vf)[BS / 4]) {
     const uint16_t* Vp = Kp + BS * D;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t)
+    for (int t = 0; t < TILES; ++t) {
+      // with P V on MFMA, row col of tile t is token 8*(col/4) + 4t + col%4,
+      // so that quad q's logits cover the consecutive tokens 8q .. 8q+7
+      const int krow = PVM ? 8 * (col >> 2) + 4 * t + (col & 3) : t * 16 + col;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        kf[t][m] = load16(Kp + (t * 16 + col) * D + m * 32 + quad * 8);
+      for (int m = 0; m < 4; ++m) kf[t][m] = load16(Kp + krow * D + m * 32 + quad * 8);
+    }
 #pragma unroll
     for (int k = 0; k < BS / 4; ++k) vf[k] = load16(Vp + (quad + 4 * k) * D + col * 8);
   };
@@ -212,7 +246,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
           for (int m = 0; m < 4; ++m) acc = mfma16x16x32<BF16>(kf[t][m], qf[m], acc);
   #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int tok = t * 16 + quad * 4 + v;
+            const int tok = PVM ? 8 * quad + 4 * t + v : t * 16 + quad * 4 + v;
             z[t][v] = tok < n_valid ? acc[v] * a.scale_log2 : -INFINITY;
           }
         }
@@ -227,25 +261,84 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         const float alpha = exp2f(m_run - m_new);
         float ps = 0.f;
         wave_sync_lds();
+        if constexpr (PVM) {
+          // P as the A operand, hi + lo halves (bf16: ~16 significant bits
+          // together; fp16: scaled by 2^15 first so small weights keep their
+          // bits, undone when the wave's result is written)
+          uint32_t hi[8], lo[8];
   #pragma unroll
-        for (int t = 0; t < TILES; ++t)
+          for (int t = 0; t < TILES; ++t)
   #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float p = exp2f(z[t][v] - m_new);
-            ps += p;
-            if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
+            for (int v = 0; v < 4; ++v) {
+              const float p = exp2f(z[t][v] - m_new);
+              ps += p;
+              const float pa = col < G ? (BF16 ? p : p * 32768.f) : 0.f;
+              const int j = 4 * t + v;
+              if constexpr (BF16) {
+                hi[j] = bf16_rne(pa);
+                lo[j] = bf16_rne(pa - __uint_as_float(hi[j] << 16));
+              } else {
+                const _Float16 h16 = (_Float16)pa;
+                hi[j] = __builtin_bit_cast(uint16_t, h16);
+                lo[j] = __builtin_bit_cast(uint16_t, (_Float16)(pa - (float)h16));
+              }
+            }
+          const uint4 a_hi = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16,
+                                        hi[6] | hi[7] << 16);
+          const uint4 a_lo = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16,
+                                        lo[6] | lo[7] << 16);
+          ps += __shfl_xor(ps, 16);
+          ps += __shfl_xor(ps, 32);
+          l_run = l_run * alpha + ps;
+          m_run = m_new;
+          if (quad == 0) alpha_s[wave][col] = alpha;  // every column: rows >= G stay finite
+          // V tile into LDS, rows of VS elements (8-byte stores: VS*2 is 8-aligned)
+  #pragma unroll
+          for (int k = 0; k < BS / 4; ++k) {
+            uint2* dst = reinterpret_cast<uint2*>(&v_s[wave][(quad + 4 * k) * VS + col * 8]);
+            dst[0] = make_uint2(vf[k].x, vf[k].y);
+            dst[1] = make_uint2(vf[k].z, vf[k].w);
           }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        l_run = l_run * alpha + ps;
-        m_run = m_new;
-        if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
-        wave_sync_lds();
+          wave_sync_lds();
+          const float al0 = alpha_s[wave][quad * 4], al1 = alpha_s[wave][quad * 4 + 1];
+          const float al2 = alpha_s[wave][quad * 4 + 2], al3 = alpha_s[wave][quad * 4 + 3];
+          const uint16_t* vcol = &v_s[wave][(8 * quad) * VS + col];
   #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float al = alpha_s[wave][h];
+          for (int c = 0; c < 8; ++c) {
+            // B operand: V[8*quad + j][c*16 + col], j = 0..7
+            uint32_t b[8];
   #pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] *= al;
+            for (int j = 0; j < 8; ++j) b[j] = vcol[j * VS + c * 16];
+            const uint4 bv = make_uint4(b[0] | b[1] << 16, b[2] | b[3] << 16, b[4] | b[5] << 16,
+                                        b[6] | b[7] << 16);
+            oc[c][0] *= al0;
+            oc[c][1] *= al1;
+            oc[c][2] *= al2;
+            oc[c][3] *= al3;
+            oc[c] = mfma16x16x32<BF16>(a_hi, bv, oc[c]);
+            oc[c] = mfma16x16x32<BF16>(a_lo, bv, oc[c]);
+          }
+        } else {
+  #pragma unroll
+          for (int t = 0; t < TILES; ++t)
+  #pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float p = exp2f(z[t][v] - m_new);
+              ps += p;
+              if (col < G) p_s[wave][t * 16 + quad * 4 + v][col] = p;
+            }
+          ps += __shfl_xor(ps, 16);
+          ps += __shfl_xor(ps, 32);
+          l_run = l_run * alpha + ps;
+          m_run = m_new;
+          if (quad == 0 && col < G) alpha_s[wave][col] = alpha;
+          wave_sync_lds();
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float al = alpha_s[wave][h];
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= al;
+          }
         }
       } else {
         // z[t][h]: logit of token t*16 + col for head h, partial over the
@@ -290,16 +383,18 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
         }
         wave_sync_lds();
       }
+      if constexpr (!PVM) {
   #pragma unroll
-      for (int k = 0; k < BS / 4; ++k) {
-        float vv[8];
-        unpack8<BF16>(vf[k], vv);
-        const int t = quad + 4 * k;
+        for (int k = 0; k < BS / 4; ++k) {
+          float vv[8];
+          unpack8<BF16>(vf[k], vv);
+          const int t = quad + 4 * k;
   #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = p_s[wave][t][h];
+          for (int h = 0; h < G; ++h) {
+            const float p = p_s[wave][t][h];
   #pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+            for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vv[e], o[h][e]);
+          }
         }
       }
   };
@@ -320,29 +415,43 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
     }
   }
 
-  // sum the four token groups of the wave
+  if constexpr (PVM) {
+    // the MFMA accumulators already sum every token of the wave
+    const float osc = BF16 ? 1.f : 1.f / 32768.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      o[h][e] += __shfl_xor(o[h][e], 16);
-      o[h][e] += __shfl_xor(o[h][e], 32);
+      for (int i = 0; i < 4; ++i)
+        if (quad * 4 + i < G) wo[wave][quad * 4 + i][c * 16 + col] = oc[c][i] * osc;
+    if (quad == 0 && col < G) {
+      wm[wave][col] = m_run;
+      wl[wave][col] = l_run;
     }
-  if (quad == 0) {
+  } else {
+    // sum the four token groups of the wave
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) wo[wave][h][col * 8 + e] = o[h][e];
-    if constexpr (MFMA) {
-      if (col < G) {
-        wm[wave][col] = m_run;
-        wl[wave][col] = l_run;
+      for (int e = 0; e < 8; ++e) {
+        o[h][e] += __shfl_xor(o[h][e], 16);
+        o[h][e] += __shfl_xor(o[h][e], 32);
       }
-    } else if (col == 0) {
+    if (quad == 0) {
 #pragma unroll
-      for (int h = 0; h < GV; ++h) {
-        wm[wave][h] = mh[h];
-        wl[wave][h] = lh[h];
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wo[wave][h][col * 8 + e] = o[h][e];
+      if constexpr (MFMA) {
+        if (col < G) {
+          wm[wave][col] = m_run;
+          wl[wave][col] = l_run;
+        }
+      } else if (col == 0) {
+#pragma unroll
+        for (int h = 0; h < GV; ++h) {
+          wm[wave][h] = mh[h];
+          wl[wave][h] = lh[h];
+        }
       }
     }
   }

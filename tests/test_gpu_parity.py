@@ -764,3 +764,29 @@ def test_staged_recall_back_to_back_calls(mode):
         H.log(f"  {call + 1} calls checked")
     finally:
         H.destroy(c)
+
+
+@pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
+@pytest.mark.parametrize("Hq", [64, 128])
+def test_attention_pv_on_matrix_cores(dtype, Hq):
+    """P V on the matrix cores (8 and 16 query heads per KV head, 32-token
+    blocks) in both storage types, SoloHead and headwise, with a ragged last
+    block; then a selection of every block of a 12,000-token context, whose
+    many small softmax weights are what the fp16 operand's 2^15 scaling
+    keeps from underflowing."""
+    H.log(f"[pv mfma] dtype {dtype} Hq {Hq}")
+    s = synth.spec(2, B=2, Hq=Hq, Hkv=8, dtype=dtype, ctx=2500, k=14, hot=6, headwise=True)
+    c, sl = _case(s, [0])
+    try:
+        for mode in (kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE):
+            _, err = _full_check(c, sl, 0, mode, kv.KVOFF_ENGINE_ZEROCOPY)
+            H.log(f"  mode {mode} attention err {err}")
+    finally:
+        H.destroy(c)
+    s = synth.spec(2, B=1, Hq=Hq, Hkv=8, dtype=dtype, ctx=12000, k=400, hot=6)
+    c, sl = _case(s, [0])
+    try:
+        _, err = _full_check(c, sl, 0, kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY)
+        H.log(f"  every block of 12,000 tokens: attention err {err}")
+    finally:
+        H.destroy(c)
