@@ -822,7 +822,7 @@ def main():
     outs = [torch.empty_like(bufs.out) for _ in layers]
     copy = torch.cuda.Stream()
 
-    def step_all(timing=False, n_layers=None):
+    def step_all(timing=False, n_layers=None, cs=None):
         return kv.kvoff_step(
             case.ctx, layer_begin=0, layer_end=n_layers or len(layers), req_ids=case.rids,
             topk=topk, mode=mode, engine=engine, k_stride=case.k_stride,
@@ -831,13 +831,14 @@ def main():
             recall_base_slot=case.recall_base, scores=[b.scores for b in sets],
             sel_idx=[b.sel_idx for b in sets], sel_cnt=[b.sel_cnt for b in sets],
             block_table=[b.table for b in sets], scale=scale, out=outs, ws=bufs.ws,
-            compute_stream=stream, copy_stream=copy, want_timing=timing)
+            compute_stream=cs or stream, copy_stream=copy, want_timing=timing)
 
     def run_steps(n):
         for n_layers in step_calls(n, len(layers)):
             step_all(n_layers=n_layers)
 
     steps_timed, warm_timed = args.steps, args.warmup
+    graph_replay = None
     if args.no_overlap:
         ms_per_step = serial_ms
     else:
@@ -858,6 +859,30 @@ def main():
             rec_sum += t["recall_ms"]
             rec_n += t["recalls"]
         rec_ms_step = rec_sum / rec_n
+        # the same schedule replayed from a HIP graph: one kvoff_step call
+        # over the layers, captured once on its compute stream (the copy
+        # streams join through the step's events).  Zero-copy engine only:
+        # the copy engines synchronise the host inside the call.
+        if engine == kv.KVOFF_ENGINE_ZEROCOPY:
+            gs = torch.cuda.Stream()
+            step_all(cs=gs)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                step_all(cs=gs)
+            torch.cuda.synchronize()
+            for _ in range(max(1, args.warmup // len(layers))):
+                g.replay()
+            torch.cuda.synchronize()
+            t_g = time.perf_counter()
+            for _ in range(n_calls):
+                g.replay()
+            torch.cuda.synchronize()
+            graph_ms = (time.perf_counter() - t_g) * 1e3 / (n_calls * len(layers))
+            graph_replay = {"layer_steps_per_s": round(1e3 / graph_ms, 3), "ms_per_step": round(graph_ms, 4),
+                            "how": f"one kvoff_step call over the {len(layers)} layers captured into a HIP "
+                                   f"graph, replayed {n_calls} times"}
+            del g
 
     # algorithmic bytes per layer-step
     rec_bytes = kv.kvoff_record_bytes(case.ctx)
@@ -944,6 +969,8 @@ def main():
         "hbm_copy_gbps_measured": round(hbm_copy, 1),
         "hbm_read_gbps_measured": round(hbm_read, 1),
     }
+    if not args.no_overlap and graph_replay is not None:
+        result["graph_replay"] = graph_replay
     result["offload_setup"] = offload_timing(case, sp, inputs, B)
     if keep_cpu:
         log("timing the oracle on host cores")

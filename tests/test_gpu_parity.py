@@ -790,3 +790,60 @@ def test_attention_pv_on_matrix_cores(dtype, Hq):
         H.log(f"  every block of 12,000 tokens: attention err {err}")
     finally:
         H.destroy(c)
+
+
+def test_step_graph_replay():
+    """kvoff_step (zero-copy recall, no stats or timing) captured into a HIP
+    graph on its compute stream; its two copy streams join the capture
+    through the step's own events.  Four replays, each after eager work on
+    the same buffers and a synchronisation, each give the eager outputs bit
+    for bit."""
+    H.log("[step graph]")
+    layers = list(range(MULTI.L))
+    c, sl = _case(MULTI, layers)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        sets = [H.make_buffers(c, mode) for _ in range(2)]
+        outs = {l: torch.empty((c.B, MULTI.Hq, MULTI.d), dtype=torch.float32, device="cuda")
+                for l in layers}
+        compute, copy, copy2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+
+        def step(n_layers):
+            return kv.kvoff_step(
+                c.ctx, layer_begin=0, layer_end=n_layers, req_ids=c.rids,
+                topk=[rq.k for rq in c.reqs], mode=mode, engine=kv.KVOFF_ENGINE_ZEROCOPY,
+                k_stride=c.k_stride, q=[c.q[l] for l in layers],
+                digest=[c.digest[l] for l in layers], digest_stride=c.nb_max, slot_pool=c.pool,
+                n_slots=c.n_slots, recall_base_slot=c.recall_base,
+                scores=[b.scores for b in sets], sel_idx=[b.sel_idx for b in sets],
+                sel_cnt=[b.sel_cnt for b in sets], block_table=[b.table for b in sets],
+                scale=1.0 / math.sqrt(MULTI.d), out=[outs[l] for l in layers], ws=sets[0].ws,
+                compute_stream=compute, copy_stream=copy, copy_stream2=copy2)
+
+        step(len(layers))
+        torch.cuda.synchronize()
+        eager = {l: outs[l].cpu().numpy().copy() for l in layers}
+        for l in layers:
+            P.check_attention_close(eager[l], P.oracle_attention(c, l, mode, sl), f"layer {l}")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=compute):
+            step(len(layers))
+        torch.cuda.synchronize()
+        for rep in range(4):
+            # eager work between replays: a shorter step over the same
+            # buffers, then the outputs poisoned
+            step(2)
+            torch.cuda.synchronize()
+            for o in outs.values():
+                o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for l in layers:
+                assert np.array_equal(outs[l].cpu().numpy().view(np.uint32),
+                                      eager[l].view(np.uint32)), (rep, l)
+        H.log("  4 replays bit-identical to the eager step")
+        del g
+    finally:
+        torch.cuda.synchronize()
+        H.destroy(c)
