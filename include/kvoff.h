@@ -289,7 +289,15 @@ size_t kvoff_workspace_size(const kvoff_ctx* ctx, int32_t call, int32_t n_req,
  * the guide's one-layer-ahead prefetch, section "The Fallacy of Naive
  * Offloading", and of its layer-wise scheduling).  With copy_stream equal to
  * compute_stream the layers run serially.  Outputs equal a serial run bit
- * for bit. */
+ * for bit.
+ * A call can be captured into a HIP graph on its compute stream (stream
+ * capture; the copy streams join it through the call's own events) when the
+ * engine is KVOFF_ENGINE_ZEROCOPY and stats and timing are NULL: the
+ * captured work then holds no host synchronisation and no memset.  Replays
+ * reuse the pointers and host arguments of the captured call (the inputs at
+ * those addresses may change between replays); one context's captured
+ * steps must not overlap each other or its eager calls, since they share its
+ * events and counters. */
 typedef struct kvoff_step_args {
   int32_t layer_begin, layer_end;
   int32_t n_req;
