@@ -40,9 +40,9 @@ METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM 
 # workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
 # and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
 # the recall source it was taken with: reported as null once that changes.
-GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65610.38, "write_kib": 131076.13,
+GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65610.98, "write_kib": 131076.03,
               "fetch_scale": 1.9999, "write_scale": 1.0000,
-              "recall_src_sha256": "847b141b6eae8f4e0c4e8aa3ab4edc1549977f13a0a6f0c3dd3d2531b6e04a35"}
+              "recall_src_sha256": "e4f84d2d465c8c7cb8540f214126917d14080726170791c7d2ae292955dcde73"}
 
 
 def gather_traffic_bytes(workload, layers):

@@ -183,16 +183,19 @@ __global__ __launch_bounds__(256) void probe_kernel(const uint4* src, int64_t n1
 }
 
 // KVOFF_GATHER_NT: bit 0 = nontemporal host loads, bit 1 = nontemporal HBM
-// stores.  Default 0: neither changes the link rate (56.9 GB/s measured
-// either way) and nontemporal stores keep the records out of L2, which the
-// attention that follows would otherwise hit.
+// stores; unset = decided per call (see launch_gather).  Neither changes the
+// link rate (56.9 GB/s measured either way).
 int gather_nt() {
   static int v = [] {
     const char* e = std::getenv("KVOFF_GATHER_NT");
-    return e ? (std::atoi(e) & 3) : 0;
+    return e ? (std::atoi(e) & 3) : -1;
   }();
   return v;
 }
+
+// Above this many bytes a recall cannot stay in the 256 MB MALL for the
+// attention that reads it next.
+constexpr int64_t kMallBytes = 256ll << 20;
 
 int gather_grid_cap() {
   static int cap = [] {
@@ -246,7 +249,18 @@ int launch_gather(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, 
   if (a.n_pieces == 0) return KVOFF_OK;
   const int64_t cap = gather_grid_cap();
   const unsigned grid = (unsigned)(a.n_pieces < cap ? a.n_pieces : cap);
-  switch (gather_nt()) {
+  int nt = gather_nt();
+  if (nt < 0) {
+    // Plain stores leave the recalled records in the caches for the
+    // attention that follows, which pays off while they fit the MALL
+    // (Llama-3-8B layer, 128 MiB: attention 32 us, 36 us after nontemporal
+    // stores).  A larger recall evicts its own dirty lines, and the
+    // attention pays for the write-backs: nontemporal stores then (the
+    // variable-recall layer, 968 MB: attention 245 -> 220 us).  The bound
+    // is every entry missing.
+    nt = a.n_pieces * a.piece_bytes > kMallBytes ? 2 : 0;
+  }
+  switch (nt) {
     case 1: hipLaunchKernelGGL((gather_kernel<true, false>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
     case 2: hipLaunchKernelGGL((gather_kernel<false, true>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
     case 3: hipLaunchKernelGGL((gather_kernel<true, true>), dim3(grid), dim3(GATHER_THREADS), 0, stream, a); break;
