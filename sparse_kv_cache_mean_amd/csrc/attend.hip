@@ -520,15 +520,18 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, fl
 }
 
 // blocks per wave (at most 4: the per-wave index cache); KVOFF_ATT_BPW
-// overrides the default for tuning sweeps
-int attend_bpw(int32_t k_stride) {
+// overrides the default for tuning sweeps.  Measured at the Llama-3-8B
+// layer's records (k_stride 64): G = 4 equal with 2 and 4 (24.4 us), G = 8
+// 28.0 -> 25.3 us and G = 16 30.8 -> 26.6 us with 4; short selections of
+// the latency-bound small shapes keep 2 (shorter chains per wave).
+int attend_bpw(int32_t k_stride, int G) {
   static const int forced = [] {
     const char* e = std::getenv("KVOFF_ATT_BPW");
     const int v = e ? std::atoi(e) : 0;
     return v >= 1 && v <= 4 ? v : 0;
   }();
   if (forced) return forced;
-  return k_stride <= 128 ? 2 : 4;
+  return k_stride <= 128 && G < 8 ? 2 : 4;
 }
 
 template <int G, int BS, bool MFMA>
@@ -557,13 +560,13 @@ void launch_g(const AttendArgs& a, int bs, bool bf16, bool mfma, dim3 grid, hipS
 
 }  // namespace
 
-int attend_splits(int32_t k_stride) {
-  const int per = ATT_WAVES * attend_bpw(k_stride);
+int attend_splits(int32_t k_stride, int G) {
+  const int per = ATT_WAVES * attend_bpw(k_stride, G);
   return (k_stride + per - 1) / per;
 }
 
 size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride) {
-  return (size_t)n_req * ctx->cfg.num_q_heads * attend_splits(k_stride) * PART * sizeof(float);
+  return (size_t)n_req * ctx->cfg.num_q_heads * attend_splits(k_stride, ctx->G) * PART * sizeof(float);
 }
 
 int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,
@@ -581,8 +584,8 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   a.part = (float*)ws;
   a.slice_bytes = ctx->slice_bytes;
   a.k_stride = k_stride;
-  a.bpw = attend_bpw(k_stride);
-  a.S = attend_splits(k_stride);
+  a.bpw = attend_bpw(k_stride, ctx->G);
+  a.S = attend_splits(k_stride, ctx->G);
   a.Hq = ctx->cfg.num_q_heads;
   a.Hkv = ctx->cfg.num_kv_heads;
   a.hw = mode == KVOFF_HEADWISE;
