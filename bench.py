@@ -835,6 +835,16 @@ def main():
     sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    # 1b) per-kernel durations: more serial layer-steps with start and stop
+    #     events bound to each kernel's own dispatch (kvoff_set_kernel_timing)
+    kv.kvoff_set_kernel_timing(case.ctx, True)
+    n_kt = min(args.steps, 20)
+    kt = []
+    for i in range(n_kt):
+        one_step(args.warmup + args.steps + i)
+        kt.append(kv.kvoff_get_kernel_times(case.ctx))
+    kv.kvoff_set_kernel_timing(case.ctx, False)
+    kern_ms = {k: float(np.mean([t[k] for t in kt])) for k in kt[0]}
 
     # 2) the headline: kvoff_step over the rotating layers, recall of layer
     #    l+1 on the copy streams under select/attention of layer l; one call
@@ -913,6 +923,18 @@ def main():
     recall_bytes = K_tot * rec_bytes
     ws_bytes = kv.kvoff_workspace_size(case.ctx, kv.KVOFF_CALL_SPARSE_DECODE, B, case.k_stride, mode)
     attend_bytes = K_tot * rec_bytes + B * sp.Hq * sp.d * (sp.es + 4) + 2 * ws_bytes
+    # the attention kernel alone: records and queries read, split partials
+    # written (the whole workspace when every split has blocks, as here)
+    attend_kernel_bytes = K_tot * rec_bytes + B * sp.Hq * sp.d * sp.es + ws_bytes
+
+    def kernel_entry(name, nbytes=None):
+        ms = kern_ms[name]
+        e = {"avg_us": round(ms * 1e3, 2)}
+        if nbytes is not None:
+            gbps = nbytes / (ms * 1e-3) / 1e9
+            e.update({"algorithmic_bytes": nbytes, "hbm_gbps": round(gbps, 1),
+                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)})
+        return e
 
     # The roofline takes the gather as it runs alone (serial order, one
     # stream).  In the kvoff_step schedule the recalls of consecutive layers
@@ -979,6 +1001,14 @@ def main():
                        "algorithmic_bytes": attend_bytes,
                        "hbm_gbps": round(attend_bytes / (att_ms * 1e-3) / 1e9, 1),
                        "frac_of_hbm_peak": round(attend_bytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        },
+        "kernels": {
+            "score_kernel": kernel_entry("score_ms", score_bytes),
+            "topk_kernel": kernel_entry("topk_ms"),
+            "attend_kernel": kernel_entry("attend_ms", attend_kernel_bytes),
+            "combine_kernel": kernel_entry("combine_ms"),
+            "how": f"start/stop events bound to each kernel's dispatch (kvoff_set_kernel_timing), "
+                   f"serial order on one stream, mean of {n_kt} layer-steps",
         },
         "serial_one_stream": {"layer_steps_per_s": round(1e3 / serial_ms, 3),
                               "ms_per_step": round(serial_ms, 4),

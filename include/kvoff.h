@@ -434,6 +434,30 @@ int kvoff_release_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, uint8_
 
 /* ------------------------------------------------------------- diagnostics */
 
+/* Per-kernel durations of the last timed kvoff_select and kvoff_sparse_decode
+ * calls (also those made inside kvoff_step), in milliseconds, from start and
+ * stop events bound to each kernel's own dispatch. */
+typedef struct kvoff_kernel_times {
+  double score_ms;   /* score kernel of the last kvoff_select             */
+  double topk_ms;    /* its top-k kernel                                   */
+  double attend_ms;  /* attention kernel of the last kvoff_sparse_decode  */
+  double combine_ms; /* its split merge                                    */
+} kvoff_kernel_times;
+
+/* Turns per-kernel timing on (on != 0) or off for later calls on this
+ * context.  While on, each kernel of kvoff_select and kvoff_sparse_decode is
+ * launched with a start and a stop event (the context's own; the first call
+ * that turns timing on creates them), which a call captured into a HIP
+ * graph must not hold: switch timing off before capturing.  Results are
+ * unchanged.  Turning it off or on again forgets the previous times.
+ * Errors: EINVAL, EHIP. */
+int kvoff_set_kernel_timing(kvoff_ctx* ctx, int32_t on);
+
+/* Waits for the stop events of the last timed calls and fills *t; the
+ * fields of a call not made since timing was turned on are 0.
+ * Errors: EINVAL, EHIP. */
+int kvoff_get_kernel_times(kvoff_ctx* ctx, kvoff_kernel_times* t);
+
 /* Reads n_bytes (a multiple of 4096) at ptr with a GPU kernel and writes an
  * XOR reduction to dev_sink (>= 4096 bytes).  ptr is device memory or pinned
  * host memory from hipHostMalloc (read over the host link through its mapped

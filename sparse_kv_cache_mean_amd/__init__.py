@@ -37,7 +37,8 @@ EXPORTS = (
     "kvoff_host_record", "kvoff_offload_blocks", "kvoff_select", "kvoff_recall",
     "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_read",
     "kvoff_strerror", "kvoff_last_error", "kvoff_admission_defaults", "kvoff_admission_plan",
-    "kvoff_make_resident", "kvoff_release_resident",
+    "kvoff_make_resident", "kvoff_release_resident", "kvoff_set_kernel_timing",
+    "kvoff_get_kernel_times",
 )
 
 
@@ -103,6 +104,14 @@ class kvoff_step_timing(ctypes.Structure):
         return {k: (int if k == "recalls" else float)(getattr(self, k)) for k, _ in self._fields_}
 
 
+class kvoff_kernel_times(ctypes.Structure):
+    _fields_ = [("score_ms", ctypes.c_double), ("topk_ms", ctypes.c_double),
+                ("attend_ms", ctypes.c_double), ("combine_ms", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {k: float(getattr(self, k)) for k, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -140,6 +149,8 @@ def lib() -> ctypes.CDLL:
     L.kvoff_admission_plan.argtypes = [P(kvoff_admission_policy), i32, ctypes.c_double, _vp, P(i32)]
     L.kvoff_make_resident.argtypes = [_vp, i32, i32, _vp, i64, i64, _vp, _vp, _vp]
     L.kvoff_release_resident.argtypes = [_vp, i32, i32, _vp, _vp]
+    L.kvoff_set_kernel_timing.argtypes = [_vp, i32]
+    L.kvoff_get_kernel_times.argtypes = [_vp, P(kvoff_kernel_times)]
     L.kvoff_strerror.argtypes = [ctypes.c_int]
     L.kvoff_strerror.restype = ctypes.c_char_p
     L.kvoff_last_error.argtypes = []
@@ -148,7 +159,7 @@ def lib() -> ctypes.CDLL:
                  "kvoff_set_consensus_lambda", "kvoff_set_attention_qk",
                  "kvoff_offload_blocks", "kvoff_select", "kvoff_recall", "kvoff_sparse_decode",
                  "kvoff_step", "kvoff_probe_read", "kvoff_attention_mass", "kvoff_admission_plan", "kvoff_make_resident",
-                 "kvoff_release_resident"):
+                 "kvoff_release_resident", "kvoff_set_kernel_timing", "kvoff_get_kernel_times"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -212,6 +223,16 @@ def kvoff_set_consensus_lambda(ctx: int, lam: float) -> None:
 
 def kvoff_set_attention_qk(ctx: int, qk: int) -> None:
     _check(lib().kvoff_set_attention_qk(ctx, qk))
+
+
+def kvoff_set_kernel_timing(ctx: int, on: bool) -> None:
+    _check(lib().kvoff_set_kernel_timing(ctx, 1 if on else 0))
+
+
+def kvoff_get_kernel_times(ctx: int) -> dict:
+    t = kvoff_kernel_times()
+    _check(lib().kvoff_get_kernel_times(ctx, ctypes.byref(t)))
+    return t.as_dict()
 
 
 def kvoff_register_request(ctx: int, n_tokens: int) -> int:

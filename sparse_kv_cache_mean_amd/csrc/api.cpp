@@ -161,6 +161,8 @@ int kvoff_destroy(kvoff_ctx* ctx) {
     for (hipEvent_t e : ctx->ev_group) (void)hipEventDestroy(e);
     for (hipEvent_t e : ctx->ev_timing) (void)hipEventDestroy(e);
     if (ctx->copy2) (void)hipStreamDestroy(ctx->copy2);
+    for (hipEvent_t e : ctx->kt_ev)
+      if (e) (void)hipEventDestroy(e);
     if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
     if (ctx->stage_buf) (void)hipHostFree(ctx->stage_buf);
     if (ctx->table_host) (void)hipHostFree(ctx->table_host);
@@ -294,9 +296,13 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
     hipStream_t s = (hipStream_t)stream;
     st = launch_score(ctx, b, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
     if (st) return st;
+    ctx->kt_recorded[KT_SCORE] |= ctx->kernel_timing;
     // consensus selections use the layout of their scope (shared or per KV head)
-    return launch_topk(ctx, b, topk, layout_of(mode), scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
-                       k_stride, s);
+    st = launch_topk(ctx, b, topk, layout_of(mode), scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
+                     k_stride, s);
+    if (st) return st;
+    ctx->kt_recorded[KT_TOPK] |= ctx->kernel_timing;
+    return KVOFF_OK;
   });
 }
 
@@ -394,8 +400,12 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
     if (need > 0 && (!ws_dev || ws_bytes < need))
       return fail(KVOFF_ERANGE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
     KVOFF_HIP(hipSetDevice(ctx->device));
-    return launch_attend(ctx, b, mode, q_dev, slot_pool_dev, block_table_dev, sel_idx_dev,
-                         sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
+    st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, block_table_dev, sel_idx_dev,
+                       sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
+    if (st) return st;
+    ctx->kt_recorded[KT_ATTEND] |= ctx->kernel_timing;
+    ctx->kt_recorded[KT_COMBINE] |= ctx->kernel_timing;
+    return KVOFF_OK;
   });
 }
 
@@ -420,6 +430,39 @@ int kvoff_attention_mass(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int
     KVOFF_HIP(hipSetDevice(ctx->device));
     return launch_mass(ctx, b, layer, mode, q_dev, sel_idx_dev, sel_cnt_dev, k_stride, scale,
                        mass_dev, (hipStream_t)stream);
+  });
+}
+
+int kvoff_set_kernel_timing(kvoff_ctx* ctx, int32_t on) {
+  return guarded([&]() -> int {
+    if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
+    if (on) {
+      KVOFF_HIP(hipSetDevice(ctx->device));
+      for (hipEvent_t& e : ctx->kt_ev)
+        if (!e) KVOFF_HIP(hipEventCreate(&e));
+    }
+    ctx->kernel_timing = on != 0;
+    for (bool& r : ctx->kt_recorded) r = false;
+    return KVOFF_OK;
+  });
+}
+
+int kvoff_get_kernel_times(kvoff_ctx* ctx, kvoff_kernel_times* t) {
+  return guarded([&]() -> int {
+    if (!ctx || !t) return fail(KVOFF_EINVAL, "ctx and t must be non-NULL");
+    double ms[KT_N] = {0.0, 0.0, 0.0, 0.0};
+    for (int k = 0; k < KT_N; ++k) {
+      if (!ctx->kt_recorded[k]) continue;
+      float v = 0.f;
+      KVOFF_HIP(hipEventSynchronize(ctx->kt_ev[2 * k + 1]));
+      KVOFF_HIP(hipEventElapsedTime(&v, ctx->kt_ev[2 * k], ctx->kt_ev[2 * k + 1]));
+      ms[k] = v;
+    }
+    t->score_ms = ms[KT_SCORE];
+    t->topk_ms = ms[KT_TOPK];
+    t->attend_ms = ms[KT_ATTEND];
+    t->combine_ms = ms[KT_COMBINE];
+    return KVOFF_OK;
   });
 }
 

@@ -535,27 +535,27 @@ int attend_bpw(int32_t k_stride, int G) {
 }
 
 template <int G, int BS, bool MFMA>
-void launch_g_bs_qk(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s) {
+void launch_g_bs_qk(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s, KEv ev) {
   if (bf16)
-    hipLaunchKernelGGL((attend_kernel<G, BS, true, MFMA>), grid, dim3(256), 0, s, a);
+    KVOFF_LAUNCH(ev, (attend_kernel<G, BS, true, MFMA>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attend_kernel<G, BS, false, MFMA>), grid, dim3(256), 0, s, a);
+    KVOFF_LAUNCH(ev, (attend_kernel<G, BS, false, MFMA>), grid, dim3(256), 0, s, a);
 }
 
 template <int G, int BS>
-void launch_g_bs(const AttendArgs& a, bool bf16, bool mfma, dim3 grid, hipStream_t s) {
+void launch_g_bs(const AttendArgs& a, bool bf16, bool mfma, dim3 grid, hipStream_t s, KEv ev) {
   if constexpr (G <= 8) {  // kvoff_set_attention_qk admits VALU only for G <= 8
-    if (!mfma) return launch_g_bs_qk<G, BS, false>(a, bf16, grid, s);
+    if (!mfma) return launch_g_bs_qk<G, BS, false>(a, bf16, grid, s, ev);
   }
-  launch_g_bs_qk<G, BS, true>(a, bf16, grid, s);
+  launch_g_bs_qk<G, BS, true>(a, bf16, grid, s, ev);
 }
 
 template <int G>
-void launch_g(const AttendArgs& a, int bs, bool bf16, bool mfma, dim3 grid, hipStream_t s) {
+void launch_g(const AttendArgs& a, int bs, bool bf16, bool mfma, dim3 grid, hipStream_t s, KEv ev) {
   if (bs == 16)
-    launch_g_bs<G, 16>(a, bf16, mfma, grid, s);
+    launch_g_bs<G, 16>(a, bf16, mfma, grid, s, ev);
   else
-    launch_g_bs<G, 32>(a, bf16, mfma, grid, s);
+    launch_g_bs<G, 32>(a, bf16, mfma, grid, s, ev);
 }
 
 }  // namespace
@@ -594,16 +594,18 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   const bool bf16 = ctx->cfg.dtype == KVOFF_BF16;
   const int bs = ctx->cfg.block_size;
   const bool mfma = ctx->attn_qk == KVOFF_QK_MFMA;
+  const KEv ev = kernel_events(ctx, KT_ATTEND);
   switch (ctx->G) {
-    case 1: launch_g<1>(a, bs, bf16, mfma, grid, stream); break;
-    case 2: launch_g<2>(a, bs, bf16, mfma, grid, stream); break;
-    case 4: launch_g<4>(a, bs, bf16, mfma, grid, stream); break;
-    case 8: launch_g<8>(a, bs, bf16, mfma, grid, stream); break;
-    default: launch_g<16>(a, bs, bf16, mfma, grid, stream); break;
+    case 1: launch_g<1>(a, bs, bf16, mfma, grid, stream, ev); break;
+    case 2: launch_g<2>(a, bs, bf16, mfma, grid, stream, ev); break;
+    case 4: launch_g<4>(a, bs, bf16, mfma, grid, stream, ev); break;
+    case 8: launch_g<8>(a, bs, bf16, mfma, grid, stream, ev); break;
+    default: launch_g<16>(a, bs, bf16, mfma, grid, stream, ev); break;
   }
   KVOFF_HIP(hipGetLastError());
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
-                     a.part, out, a.S, sel_cnt, k_stride, ATT_WAVES * a.bpw, a.Hq);
+  const KEv ev_c = kernel_events(ctx, KT_COMBINE);
+  KVOFF_LAUNCH(ev_c, combine_kernel, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
+               (const float*)a.part, out, (int)a.S, sel_cnt, (int)k_stride, ATT_WAVES * a.bpw, (int)a.Hq);
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }

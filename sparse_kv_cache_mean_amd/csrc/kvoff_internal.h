@@ -4,6 +4,7 @@
 
 #include <exception>
 #include <new>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -39,6 +40,14 @@ struct ReqHost {
 
 class StagePool;
 
+// kernels timed by kvoff_set_kernel_timing, in kvoff_kernel_times order
+enum KernelSlot { KT_SCORE = 0, KT_TOPK, KT_ATTEND, KT_COMBINE, KT_N };
+
+// start/stop events of one kernel launch; both null: an untimed launch
+struct KEv {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
 }  // namespace kvoff
 
 struct kvoff_ctx {
@@ -72,6 +81,10 @@ struct kvoff_ctx {
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
   hipStream_t copy2 = nullptr;              // kvoff_step's own second copy stream (lazy)
   bool ev_stage_pending = false;
+  // per-kernel timing (kvoff_set_kernel_timing): start/stop events per slot
+  bool kernel_timing = false;
+  hipEvent_t kt_ev[2 * kvoff::KT_N] = {};
+  bool kt_recorded[kvoff::KT_N] = {};
 };
 
 namespace kvoff {
@@ -115,6 +128,27 @@ inline int32_t layout_of(int32_t mode) {
     default: return -1;
   }
 }
+
+// the events of a kernel slot while per-kernel timing is on, else none
+inline KEv kernel_events(const kvoff_ctx* ctx, int slot) {
+  KEv e;
+  if (ctx->kernel_timing) {
+    e.start = ctx->kt_ev[2 * slot];
+    e.stop = ctx->kt_ev[2 * slot + 1];
+  }
+  return e;
+}
+
+// Launch of `kernel` on `stream`: with the start/stop events bound to the
+// dispatch itself (hipExtLaunchKernelGGL) when `ev` holds them, else plain.
+#define KVOFF_LAUNCH(ev, kernel, grid, block, lds, stream, ...)                             \
+  do {                                                                                     \
+    if ((ev).start)                                                                        \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, (ev).start, (ev).stop, 0,     \
+                            __VA_ARGS__);                                                  \
+    else                                                                                   \
+      hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                   \
+  } while (0)
 
 // check a batch and fill BatchIds; ESTATE for an unknown id
 int make_batch(const kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, BatchIds* out);

@@ -410,41 +410,41 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 }
 
 template <int KPT>
-void topk_launch(const TopkArgs& a, dim3 grid, bool hw, hipStream_t s) {
+void topk_launch(const TopkArgs& a, dim3 grid, bool hw, hipStream_t s, KEv ev) {
   if (hw)
-    hipLaunchKernelGGL((topk_kernel<true, KPT>), grid, dim3(256), 0, s, a);
+    KVOFF_LAUNCH(ev, (topk_kernel<true, KPT>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((topk_kernel<false, KPT>), grid, dim3(256), 0, s, a);
+    KVOFF_LAUNCH(ev, (topk_kernel<false, KPT>), grid, dim3(256), 0, s, a);
 }
 
 template <int NC, int MODE, bool NT>
-void score_launch_b(const ScoreArgs& a, int64_t max_nb, hipStream_t s) {
-  const size_t lds = std::max<size_t>((size_t)a.Hq * kHeadDim * 2, 4 * 256 * 16);  // staged q rows
+void score_launch_b(const ScoreArgs& a, int64_t max_nb, hipStream_t s, KEv ev) {
+  const uint32_t lds = (uint32_t)std::max<size_t>((size_t)a.Hq * kHeadDim * 2, 4 * 256 * 16);  // staged q rows
   const dim3 grid((unsigned)((max_nb + SCORE_WG_BLOCKS - 1) / SCORE_WG_BLOCKS), (unsigned)a.batch.n);
   if (a.bf16)
-    hipLaunchKernelGGL((score_kernel<NC, MODE, true, NT>), grid, dim3(256), lds, s, a);
+    KVOFF_LAUNCH(ev, (score_kernel<NC, MODE, true, NT>), grid, dim3(256), lds, s, a);
   else
-    hipLaunchKernelGGL((score_kernel<NC, MODE, false, NT>), grid, dim3(256), lds, s, a);
+    KVOFF_LAUNCH(ev, (score_kernel<NC, MODE, false, NT>), grid, dim3(256), lds, s, a);
 }
 
 template <int NC, int MODE>
-void score_launch_m(const ScoreArgs& a, int64_t max_nb, hipStream_t s) {
+void score_launch_m(const ScoreArgs& a, int64_t max_nb, hipStream_t s, KEv ev) {
   if (score_nt())
-    score_launch_b<NC, MODE, true>(a, max_nb, s);
+    score_launch_b<NC, MODE, true>(a, max_nb, s, ev);
   else
-    score_launch_b<NC, MODE, false>(a, max_nb, s);
+    score_launch_b<NC, MODE, false>(a, max_nb, s, ev);
 }
 
 template <int NC>
-void score_launch(const ScoreArgs& a, int64_t max_nb, int mode, hipStream_t s) {
+void score_launch(const ScoreArgs& a, int64_t max_nb, int mode, hipStream_t s, KEv ev) {
   if (mode == KVOFF_HEADWISE)
-    score_launch_m<NC, MODE_HEADWISE>(a, max_nb, s);
+    score_launch_m<NC, MODE_HEADWISE>(a, max_nb, s, ev);
   else if (mode == KVOFF_CONSENSUS)
-    score_launch_m<NC, MODE_CONSENSUS>(a, max_nb, s);
+    score_launch_m<NC, MODE_CONSENSUS>(a, max_nb, s, ev);
   else if (mode == KVOFF_CONSENSUS_GROUP)
-    score_launch_m<NC, MODE_GROUP>(a, max_nb, s);
+    score_launch_m<NC, MODE_GROUP>(a, max_nb, s, ev);
   else
-    score_launch_m<NC, MODE_SOLO>(a, max_nb, s);
+    score_launch_m<NC, MODE_SOLO>(a, max_nb, s, ev);
 }
 
 }  // namespace
@@ -466,12 +466,13 @@ int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t max_nb, const 
   a.lambda = ctx->consensus_lambda;
   const int F = a.Hkv * kHeadDim;
   const int NC = (F + 255) / 256;
+  const KEv ev = kernel_events(ctx, KT_SCORE);
   switch (NC) {
-    case 1: score_launch<1>(a, max_nb, mode, stream); break;
-    case 2: score_launch<2>(a, max_nb, mode, stream); break;
+    case 1: score_launch<1>(a, max_nb, mode, stream, ev); break;
+    case 2: score_launch<2>(a, max_nb, mode, stream, ev); break;
     case 3:
-    case 4: score_launch<4>(a, max_nb, mode, stream); break;
-    default: score_launch<8>(a, max_nb, mode, stream); break;
+    case 4: score_launch<4>(a, max_nb, mode, stream, ev); break;
+    default: score_launch<8>(a, max_nb, mode, stream, ev); break;
   }
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
@@ -494,14 +495,15 @@ int launch_topk(const kvoff_ctx* ctx, const BatchIds& b, const int32_t* topk_hos
   for (int i = 0; i < b.n; ++i) max_nb = std::max<int64_t>(max_nb, ctx->reqs[b.id[i]].nb);
   const bool hw = mode == KVOFF_HEADWISE;
   const dim3 grid((unsigned)(hw ? b.n * a.Hkv : b.n));
+  const KEv ev = kernel_events(ctx, KT_TOPK);
   if (max_nb <= 1024)
-    topk_launch<4>(a, grid, hw, stream);
+    topk_launch<4>(a, grid, hw, stream, ev);
   else if (max_nb <= 4096)
-    topk_launch<16>(a, grid, hw, stream);
+    topk_launch<16>(a, grid, hw, stream, ev);
   else if (max_nb <= 16384)
-    topk_launch<64>(a, grid, hw, stream);
+    topk_launch<64>(a, grid, hw, stream, ev);
   else
-    topk_launch<0>(a, grid, hw, stream);
+    topk_launch<0>(a, grid, hw, stream, ev);
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }

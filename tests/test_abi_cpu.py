@@ -70,6 +70,8 @@ def test_null_context_is_rejected():
     assert kv.lib().kvoff_register_request(None, 10, None) == kv.KVOFF_EINVAL
     assert kv.lib().kvoff_step(None, None) == kv.KVOFF_EINVAL
     assert kv.kvoff_workspace_size(None, kv.KVOFF_CALL_SPARSE_DECODE, 1, 1, 0) == 0
+    assert kv.lib().kvoff_set_kernel_timing(None, 1) == kv.KVOFF_EINVAL
+    assert kv.lib().kvoff_get_kernel_times(None, None) == kv.KVOFF_EINVAL
 
 
 def test_c_program_compiles_and_links_against_the_abi(tmp_path):

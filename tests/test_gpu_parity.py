@@ -792,6 +792,44 @@ def test_attention_pv_on_matrix_cores(dtype, Hq):
         H.destroy(c)
 
 
+def test_kernel_timing_leaves_results_unchanged():
+    """Per-kernel timing: with it on, the selection, block table, recalled
+    bytes and attention output equal an untimed run's bit for bit, and every
+    timed kernel reports a positive duration.  Switching timing off forgets
+    the times, and calls made while it is off record none."""
+    H.log("[kernel timing]")
+    s = synth.spec(2, B=3, ctx=3000, k=20, hot=6)
+    c, sl = _case(s, [0])
+    zeros = dict(score_ms=0.0, topk_ms=0.0, attend_ms=0.0, combine_ms=0.0)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        ref = H.make_buffers(c, mode)
+        H.run_layer(c, 0, mode, ref)
+        torch.cuda.synchronize()
+        kv.kvoff_set_kernel_timing(c.ctx, True)
+        assert kv.kvoff_get_kernel_times(c.ctx) == zeros
+        bufs = H.make_buffers(c, mode)
+        H.run_layer(c, 0, mode, bufs)
+        t = kv.kvoff_get_kernel_times(c.ctx)
+        torch.cuda.synchronize()
+        H.log(f"  kernel times {t}")
+        assert all(0.0 < v < 1000.0 for v in t.values()), t
+        for a, b in ((ref.sel_idx, bufs.sel_idx), (ref.sel_cnt, bufs.sel_cnt),
+                     (ref.table, bufs.table)):
+            assert torch.equal(a, b)
+        assert torch.equal(ref.out.view(torch.int32), bufs.out.view(torch.int32))
+        P.check_selection(c, 0, mode, bufs, sl)
+        P.check_recall(c, 0, mode, bufs, sl)
+        P.check_attention(c, 0, mode, bufs, sl)
+        kv.kvoff_set_kernel_timing(c.ctx, False)
+        H.run_layer(c, 0, mode, bufs)
+        torch.cuda.synchronize()
+        assert kv.kvoff_get_kernel_times(c.ctx) == zeros
+    finally:
+        torch.cuda.synchronize()
+        H.destroy(c)
+
+
 def test_step_graph_replay():
     """kvoff_step (zero-copy recall, no stats or timing) captured into a HIP
     graph on its compute stream; its two copy streams join the capture
