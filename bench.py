@@ -835,16 +835,15 @@ def main():
     sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     rec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     att_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    # 1b) per-kernel durations: more serial layer-steps with start and stop
-    #     events bound to each kernel's own dispatch (kvoff_set_kernel_timing)
+    # 1b) per-kernel durations: the serial layer-steps again, each kernel
+    #     launched with start and stop events bound to its own dispatch
+    #     (kvoff_set_kernel_timing; the library averages over the calls)
     kv.kvoff_set_kernel_timing(case.ctx, True)
-    n_kt = min(args.steps, 20)
-    kt = []
-    for i in range(n_kt):
-        one_step(args.warmup + args.steps + i)
-        kt.append(kv.kvoff_get_kernel_times(case.ctx))
+    for i in range(args.steps):
+        one_step(args.warmup + i)
+    kern_ms = kv.kvoff_get_kernel_times(case.ctx)
     kv.kvoff_set_kernel_timing(case.ctx, False)
-    kern_ms = {k: float(np.mean([t[k] for t in kt])) for k in kt[0]}
+    assert kern_ms["select_calls"] == kern_ms["decode_calls"] == args.steps, kern_ms
 
     # 2) the headline: kvoff_step over the rotating layers, recall of layer
     #    l+1 on the copy streams under select/attention of layer l; one call
@@ -1008,7 +1007,7 @@ def main():
             "attend_kernel": kernel_entry("attend_ms", attend_kernel_bytes),
             "combine_kernel": kernel_entry("combine_ms"),
             "how": f"start/stop events bound to each kernel's dispatch (kvoff_set_kernel_timing), "
-                   f"serial order on one stream, mean of {n_kt} layer-steps",
+                   f"serial order on one stream, mean of {args.steps} layer-steps",
         },
         "serial_one_stream": {"layer_steps_per_s": round(1e3 / serial_ms, 3),
                               "ms_per_step": round(serial_ms, 4),

@@ -434,28 +434,33 @@ int kvoff_release_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, uint8_
 
 /* ------------------------------------------------------------- diagnostics */
 
-/* Per-kernel durations of the last timed kvoff_select and kvoff_sparse_decode
- * calls (also those made inside kvoff_step), in milliseconds, from start and
- * stop events bound to each kernel's own dispatch. */
+/* Mean per-kernel durations of the timed kvoff_select and kvoff_sparse_decode
+ * calls (also those made inside kvoff_step) since timing was turned on, in
+ * milliseconds, from start and stop events bound to each kernel's own
+ * dispatch. */
 typedef struct kvoff_kernel_times {
-  double score_ms;   /* score kernel of the last kvoff_select             */
-  double topk_ms;    /* its top-k kernel                                   */
-  double attend_ms;  /* attention kernel of the last kvoff_sparse_decode  */
-  double combine_ms; /* its split merge                                    */
+  double score_ms;       /* score kernel of kvoff_select                     */
+  double topk_ms;        /* its top-k kernel                                  */
+  double attend_ms;      /* attention kernel of kvoff_sparse_decode          */
+  double combine_ms;     /* its split merge                                   */
+  int64_t select_calls;  /* timed kvoff_select calls the first two average   */
+  int64_t decode_calls;  /* timed kvoff_sparse_decode calls the last two average */
 } kvoff_kernel_times;
 
 /* Turns per-kernel timing on (on != 0) or off for later calls on this
- * context.  While on, each kernel of kvoff_select and kvoff_sparse_decode is
- * launched with a start and a stop event (the context's own; the first call
- * that turns timing on creates them), which a call captured into a HIP
- * graph must not hold: switch timing off before capturing.  Results are
- * unchanged.  Turning it off or on again forgets the previous times.
- * Errors: EINVAL, EHIP. */
+ * context; either way the accumulated times are cleared.  While on, each
+ * kernel of kvoff_select and kvoff_sparse_decode is launched with a start
+ * and a stop event from a ring of 64 per kernel that the context owns
+ * (created by the first call that turns timing on).  Calls do not wait for
+ * their own events: the host waits only when the ring wraps, for the events
+ * of the call 64 calls earlier.  A call captured into a HIP graph must not
+ * hold these events: switch timing off before capturing.  Results are
+ * unchanged.  Errors: EINVAL, EHIP. */
 int kvoff_set_kernel_timing(kvoff_ctx* ctx, int32_t on);
 
-/* Waits for the stop events of the last timed calls and fills *t; the
- * fields of a call not made since timing was turned on are 0.
- * Errors: EINVAL, EHIP. */
+/* Waits for the stop events of every timed call not yet accounted and fills
+ * *t with the means since timing was turned on (zeros and zero counts when
+ * no call was timed).  Errors: EINVAL, EHIP. */
 int kvoff_get_kernel_times(kvoff_ctx* ctx, kvoff_kernel_times* t);
 
 /* Reads n_bytes (a multiple of 4096) at ptr with a GPU kernel and writes an

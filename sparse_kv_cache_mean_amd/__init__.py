@@ -106,10 +106,11 @@ class kvoff_step_timing(ctypes.Structure):
 
 class kvoff_kernel_times(ctypes.Structure):
     _fields_ = [("score_ms", ctypes.c_double), ("topk_ms", ctypes.c_double),
-                ("attend_ms", ctypes.c_double), ("combine_ms", ctypes.c_double)]
+                ("attend_ms", ctypes.c_double), ("combine_ms", ctypes.c_double),
+                ("select_calls", ctypes.c_int64), ("decode_calls", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
-        return {k: float(getattr(self, k)) for k, _ in self._fields_}
+        return {k: (int if k.endswith("_calls") else float)(getattr(self, k)) for k, _ in self._fields_}
 
 
 _lib = None

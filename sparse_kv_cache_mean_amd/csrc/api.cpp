@@ -43,6 +43,29 @@ int make_batch(const kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, Batc
   return KVOFF_OK;
 }
 
+// reads the n oldest in-use event sets of a kernel slot into its sums
+static int read_pending_sets(kvoff_ctx* ctx, int slot, int n) {
+  for (; n > 0; --n) {
+    const int set = (ctx->kt_next[slot] - ctx->kt_pending[slot] + KT_RING) % KT_RING;
+    const size_t i = 2 * ((size_t)slot * KT_RING + (size_t)set);
+    float ms = 0.f;
+    KVOFF_HIP(hipEventSynchronize(ctx->kt_ev[i + 1]));
+    KVOFF_HIP(hipEventElapsedTime(&ms, ctx->kt_ev[i], ctx->kt_ev[i + 1]));
+    ctx->kt_sum_ms[slot] += ms;
+    ++ctx->kt_count[slot];
+    --ctx->kt_pending[slot];
+  }
+  return KVOFF_OK;
+}
+
+int kernel_timing_advance(kvoff_ctx* ctx, int slot) {
+  if (!ctx->kernel_timing) return KVOFF_OK;
+  ctx->kt_next[slot] = (ctx->kt_next[slot] + 1) % KT_RING;
+  ++ctx->kt_pending[slot];
+  // the next launch reuses the oldest set once every set is in use
+  return ctx->kt_pending[slot] == KT_RING ? read_pending_sets(ctx, slot, 1) : KVOFF_OK;
+}
+
 }  // namespace kvoff
 
 using namespace kvoff;
@@ -296,12 +319,12 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
     hipStream_t s = (hipStream_t)stream;
     st = launch_score(ctx, b, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
     if (st) return st;
-    ctx->kt_recorded[KT_SCORE] |= ctx->kernel_timing;
+    if ((st = kernel_timing_advance(ctx, KT_SCORE))) return st;
     // consensus selections use the layout of their scope (shared or per KV head)
     st = launch_topk(ctx, b, topk, layout_of(mode), scores_dev, digest_stride, sel_idx_dev, sel_cnt_dev,
                      k_stride, s);
     if (st) return st;
-    ctx->kt_recorded[KT_TOPK] |= ctx->kernel_timing;
+    if ((st = kernel_timing_advance(ctx, KT_TOPK))) return st;
     return KVOFF_OK;
   });
 }
@@ -403,8 +426,8 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
     st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, block_table_dev, sel_idx_dev,
                        sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
     if (st) return st;
-    ctx->kt_recorded[KT_ATTEND] |= ctx->kernel_timing;
-    ctx->kt_recorded[KT_COMBINE] |= ctx->kernel_timing;
+    if ((st = kernel_timing_advance(ctx, KT_ATTEND))) return st;
+    if ((st = kernel_timing_advance(ctx, KT_COMBINE))) return st;
     return KVOFF_OK;
   });
 }
@@ -436,13 +459,21 @@ int kvoff_attention_mass(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int
 int kvoff_set_kernel_timing(kvoff_ctx* ctx, int32_t on) {
   return guarded([&]() -> int {
     if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
-    if (on) {
+    if (on && ctx->kt_ev.empty()) {
       KVOFF_HIP(hipSetDevice(ctx->device));
-      for (hipEvent_t& e : ctx->kt_ev)
-        if (!e) KVOFF_HIP(hipEventCreate(&e));
+      ctx->kt_ev.reserve(2 * (size_t)KT_N * KT_RING);
+      while (ctx->kt_ev.size() < 2 * (size_t)KT_N * KT_RING) {
+        hipEvent_t e;
+        KVOFF_HIP(hipEventCreate(&e));
+        ctx->kt_ev.push_back(e);
+      }
     }
     ctx->kernel_timing = on != 0;
-    for (bool& r : ctx->kt_recorded) r = false;
+    for (int k = 0; k < KT_N; ++k) {
+      ctx->kt_next[k] = ctx->kt_pending[k] = 0;
+      ctx->kt_sum_ms[k] = 0.0;
+      ctx->kt_count[k] = 0;
+    }
     return KVOFF_OK;
   });
 }
@@ -450,18 +481,19 @@ int kvoff_set_kernel_timing(kvoff_ctx* ctx, int32_t on) {
 int kvoff_get_kernel_times(kvoff_ctx* ctx, kvoff_kernel_times* t) {
   return guarded([&]() -> int {
     if (!ctx || !t) return fail(KVOFF_EINVAL, "ctx and t must be non-NULL");
-    double ms[KT_N] = {0.0, 0.0, 0.0, 0.0};
     for (int k = 0; k < KT_N; ++k) {
-      if (!ctx->kt_recorded[k]) continue;
-      float v = 0.f;
-      KVOFF_HIP(hipEventSynchronize(ctx->kt_ev[2 * k + 1]));
-      KVOFF_HIP(hipEventElapsedTime(&v, ctx->kt_ev[2 * k], ctx->kt_ev[2 * k + 1]));
-      ms[k] = v;
+      int st = read_pending_sets(ctx, k, ctx->kt_pending[k]);
+      if (st) return st;
     }
+    double ms[KT_N];
+    for (int k = 0; k < KT_N; ++k)
+      ms[k] = ctx->kt_count[k] ? ctx->kt_sum_ms[k] / (double)ctx->kt_count[k] : 0.0;
     t->score_ms = ms[KT_SCORE];
     t->topk_ms = ms[KT_TOPK];
     t->attend_ms = ms[KT_ATTEND];
     t->combine_ms = ms[KT_COMBINE];
+    t->select_calls = ctx->kt_count[KT_SCORE];
+    t->decode_calls = ctx->kt_count[KT_ATTEND];
     return KVOFF_OK;
   });
 }

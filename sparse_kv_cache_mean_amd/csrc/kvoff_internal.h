@@ -40,8 +40,10 @@ struct ReqHost {
 
 class StagePool;
 
-// kernels timed by kvoff_set_kernel_timing, in kvoff_kernel_times order
+// kernels timed by kvoff_set_kernel_timing, in kvoff_kernel_times order,
+// and the event sets each keeps in its ring
 enum KernelSlot { KT_SCORE = 0, KT_TOPK, KT_ATTEND, KT_COMBINE, KT_N };
+constexpr int KT_RING = 64;
 
 // start/stop events of one kernel launch; both null: an untimed launch
 struct KEv {
@@ -81,10 +83,16 @@ struct kvoff_ctx {
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
   hipStream_t copy2 = nullptr;              // kvoff_step's own second copy stream (lazy)
   bool ev_stage_pending = false;
-  // per-kernel timing (kvoff_set_kernel_timing): start/stop events per slot
+  // per-kernel timing (kvoff_set_kernel_timing): per kernel slot a ring of
+  // KT_RING (start, stop) event pairs, [slot][set][start|stop]; sets in use
+  // are the `pending` ones before `next`; their durations, once read, go to
+  // the sums
   bool kernel_timing = false;
-  hipEvent_t kt_ev[2 * kvoff::KT_N] = {};
-  bool kt_recorded[kvoff::KT_N] = {};
+  std::vector<hipEvent_t> kt_ev;
+  int kt_next[kvoff::KT_N] = {};
+  int kt_pending[kvoff::KT_N] = {};
+  double kt_sum_ms[kvoff::KT_N] = {};
+  int64_t kt_count[kvoff::KT_N] = {};
 };
 
 namespace kvoff {
@@ -129,15 +137,20 @@ inline int32_t layout_of(int32_t mode) {
   }
 }
 
-// the events of a kernel slot while per-kernel timing is on, else none
+// the next events of a kernel slot while per-kernel timing is on, else none
 inline KEv kernel_events(const kvoff_ctx* ctx, int slot) {
   KEv e;
   if (ctx->kernel_timing) {
-    e.start = ctx->kt_ev[2 * slot];
-    e.stop = ctx->kt_ev[2 * slot + 1];
+    const size_t i = 2 * ((size_t)slot * KT_RING + (size_t)ctx->kt_next[slot]);
+    e.start = ctx->kt_ev[i];
+    e.stop = ctx->kt_ev[i + 1];
   }
   return e;
 }
+
+// after a launch that used kernel_events(ctx, slot): moves the slot's ring
+// on, first reading the oldest set when the ring is full
+int kernel_timing_advance(kvoff_ctx* ctx, int slot);
 
 // Launch of `kernel` on `stream`: with the start/stop events bound to the
 // dispatch itself (hipExtLaunchKernelGGL) when `ev` holds them, else plain.

@@ -794,13 +794,16 @@ def test_attention_pv_on_matrix_cores(dtype, Hq):
 
 def test_kernel_timing_leaves_results_unchanged():
     """Per-kernel timing: with it on, the selection, block table, recalled
-    bytes and attention output equal an untimed run's bit for bit, and every
-    timed kernel reports a positive duration.  Switching timing off forgets
-    the times, and calls made while it is off record none."""
+    bytes and attention output equal an untimed run's bit for bit, every
+    timed kernel reports a positive mean duration, and the call counts cover
+    more calls than the 64-set event ring holds (so the ring wraps).
+    Switching timing off clears the times, and calls made while it is off
+    record none."""
     H.log("[kernel timing]")
     s = synth.spec(2, B=3, ctx=3000, k=20, hot=6)
     c, sl = _case(s, [0])
-    zeros = dict(score_ms=0.0, topk_ms=0.0, attend_ms=0.0, combine_ms=0.0)
+    zeros = dict(score_ms=0.0, topk_ms=0.0, attend_ms=0.0, combine_ms=0.0, select_calls=0,
+                 decode_calls=0)
     try:
         mode = kv.KVOFF_SOLOHEAD
         ref = H.make_buffers(c, mode)
@@ -809,11 +812,14 @@ def test_kernel_timing_leaves_results_unchanged():
         kv.kvoff_set_kernel_timing(c.ctx, True)
         assert kv.kvoff_get_kernel_times(c.ctx) == zeros
         bufs = H.make_buffers(c, mode)
-        H.run_layer(c, 0, mode, bufs)
+        n_calls = 70
+        for _ in range(n_calls):
+            H.run_layer(c, 0, mode, bufs)
         t = kv.kvoff_get_kernel_times(c.ctx)
         torch.cuda.synchronize()
         H.log(f"  kernel times {t}")
-        assert all(0.0 < v < 1000.0 for v in t.values()), t
+        assert t["select_calls"] == t["decode_calls"] == n_calls, t
+        assert all(0.0 < t[k] < 1000.0 for k in ("score_ms", "topk_ms", "attend_ms", "combine_ms")), t
         for a, b in ((ref.sel_idx, bufs.sel_idx), (ref.sel_cnt, bufs.sel_cnt),
                      (ref.table, bufs.table)):
             assert torch.equal(a, b)
