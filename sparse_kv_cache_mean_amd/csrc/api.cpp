@@ -150,10 +150,8 @@ int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
       e = hipMalloc(&ctx->d_reqs, sizeof(ReqDev) * (size_t)c.max_requests);
       if (e == hipSuccess) e = hipMalloc(&ctx->d_counters, 8 * sizeof(unsigned long long));
       if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_stage, hipEventDisableTiming);
-      for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = hipEventCreateWithFlags(&ctx->ev_sel[i], hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_rec[i], hipEventDisableTiming);
-      }
       if (e != hipSuccess) {
         status = fail(KVOFF_EHIP, "context setup: %s", hipGetErrorString(e));
         break;
@@ -178,7 +176,6 @@ int kvoff_destroy(kvoff_ctx* ctx) {
     (void)hipDeviceSynchronize();
     for (int i = 0; i < 2; ++i) {
       if (ctx->ev_sel[i]) (void)hipEventDestroy(ctx->ev_sel[i]);
-      if (ctx->ev_rec[i]) (void)hipEventDestroy(ctx->ev_rec[i]);
     }
     stage_pool_destroy(ctx);
     for (hipEvent_t e : ctx->ev_group) (void)hipEventDestroy(e);

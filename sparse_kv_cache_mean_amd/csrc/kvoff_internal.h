@@ -68,8 +68,7 @@ struct kvoff_ctx {
   std::vector<uint8_t> resident;   // [req][layer]: pinned in HBM by kvoff_make_resident
   kvoff::ReqDev* d_reqs = nullptr; // device copy of the request table
   unsigned long long* d_counters = nullptr;  // recall statistics (device)
-  hipEvent_t ev_sel[2] = {nullptr, nullptr};
-  hipEvent_t ev_rec[2] = {nullptr, nullptr};
+  hipEvent_t ev_sel[2] = {nullptr, nullptr};  // selection -> recall hand-off per buffer set
   // staged (CPU gather + bulk copy) recall engine
   kvoff::StagePool* stage_pool = nullptr;  // host worker threads, created on first use
   void* stage_buf = nullptr;                // pinned staging buffer, grown on demand
