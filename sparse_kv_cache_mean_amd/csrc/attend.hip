@@ -482,7 +482,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
 
 // One workgroup per (request, head), one thread per dim: single-pass merge
 // of the request's non-empty splits in order (ceil(count / blocks per
-// split) of the S), loads batched 8 splits at a time.
+// split) of the S), loads batched NB splits at a time.
+template <int NB>
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, float* out, int S,
                                                           const int32_t* sel_cnt, int k_stride,
                                                           int per_split, int Hq) {
@@ -492,17 +493,17 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, fl
   const int cnt = min(sel_cnt[rh / Hq], k_stride);
   const int Sr = min(S, (cnt + per_split - 1) / per_split);
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < Sr; s0 += 8) {
-    float m[8], l[8], o[8];
+  for (int s0 = 0; s0 < Sr; s0 += NB) {
+    float m[NB], l[NB], o[NB];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NB; ++k) {
       const int t = min(s0 + k, Sr - 1);
       m[k] = P[t * PART];
       l[k] = P[t * PART + 1];
       o[k] = P[t * PART + 2 + j];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NB; ++k) {
       if (s0 + k >= Sr || m[k] == -INFINITY) continue;
       if (m[k] > M) {
         const float f = M == -INFINITY ? 0.f : exp2f(M - m[k]);
@@ -604,8 +605,19 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   }
   KVOFF_HIP(hipGetLastError());
   const KEv ev_c = kernel_events(ctx, KT_COMBINE);
-  KVOFF_LAUNCH(ev_c, combine_kernel, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
-               (const float*)a.part, out, (int)a.S, sel_cnt, (int)k_stride, ATT_WAVES * a.bpw, (int)a.Hq);
+  // splits merged per batch of loads: up to 32, so that a long selection
+  // (36 splits at the variable-recall layer) waits for two rounds of loads
+  // instead of five (combine 16.0 -> 12.9 us there); no more than S needs
+  const int nb = a.S > 16 ? 32 : a.S > 8 ? 16 : 8;
+  if (nb == 32)
+    KVOFF_LAUNCH(ev_c, combine_kernel<32>, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
+                 (const float*)a.part, out, (int)a.S, sel_cnt, (int)k_stride, ATT_WAVES * a.bpw, (int)a.Hq);
+  else if (nb == 16)
+    KVOFF_LAUNCH(ev_c, combine_kernel<16>, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
+                 (const float*)a.part, out, (int)a.S, sel_cnt, (int)k_stride, ATT_WAVES * a.bpw, (int)a.Hq);
+  else
+    KVOFF_LAUNCH(ev_c, combine_kernel<8>, dim3((unsigned)(b.n * a.Hq)), dim3(kHeadDim), 0, stream,
+                 (const float*)a.part, out, (int)a.S, sel_cnt, (int)k_stride, ATT_WAVES * a.bpw, (int)a.Hq);
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }
