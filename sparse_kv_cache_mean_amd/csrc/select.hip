@@ -21,11 +21,14 @@
 // (KVOFF_CONSENSUS_GROUP) each query head's sum is formed from the q rows in
 // LDS and the group's max + lambda * mean is one score per KV head.
 //
-// topk_kernel: one workgroup per request (per (request, KV head) when
-// headwise) runs an MSB-first radix select over order-preserving 64-bit keys
-// of the fp64 scores (8 passes of 8 bits, LDS histogram), then an ordered
-// compaction in block order that keeps every key above the threshold and the
-// lowest-numbered keys equal to it.  Output is ascending block ids.
+// Top-k: one workgroup per request (per (request, KV head) when headwise)
+// runs an MSB-first radix select over order-preserving 64-bit keys of the
+// fp64 scores (up to 8 passes of 8 bits, LDS histogram, stopping once the
+// threshold bucket is taken whole), then an ordered compaction in block
+// order that keeps every key above the threshold and the lowest-numbered
+// keys equal to it.  Output is ascending block ids.  topk_regs_kernel keeps
+// up to 64 keys per thread in registers (nb <= 16,384) and needs one barrier
+// per pass; topk_kernel re-reads the scores for longer contexts.
 #include <algorithm>
 #include <cstdlib>
 
@@ -289,9 +292,9 @@ __device__ __forceinline__ uint64_t score_key(double x) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// KPT > 0: each thread keeps the keys of blocks tid + 256*k (k < KPT) in
-// registers (nb <= 256*KPT); KPT == 0 re-reads the scores every pass.
-template <bool HW, int KPT>
+// Streaming top-k for long contexts (more blocks than topk_regs_kernel keeps
+// in registers): the scores are re-read from memory in every pass.
+template <bool HW>
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_digit, s_above, s_count;
@@ -308,15 +311,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunks = (nb + 255) / 256;
 
-  uint64_t keys[KPT > 0 ? KPT : 1];
-  if constexpr (KPT > 0) {
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) keys[k] = score_key(S[min(tid + 256 * k, nb - 1)]);
-  }
-  auto key_at = [&](int k) -> uint64_t {
-    if constexpr (KPT > 0) return keys[k];
-    else return score_key(S[min(tid + 256 * k, nb - 1)]);
-  };
+  auto key_at = [&](int k) -> uint64_t { return score_key(S[min(tid + 256 * k, nb - 1)]); };
 
   uint64_t prefix = 0, mask = 0;
   uint32_t need = (uint32_t)K;
@@ -324,13 +319,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     const int shift = 56 - 8 * pass;
     hist[tid] = 0;
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < (KPT > 0 ? KPT : 1); ++k) {
-      for (int kk = k; kk < (KPT > 0 ? k + 1 : chunks); ++kk) {
-        const uint64_t key = key_at(kk);
-        if (tid + 256 * kk < nb && (key & mask) == prefix)
-          atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
+    for (int kk = 0; kk < chunks; ++kk) {
+      const uint64_t key = key_at(kk);
+      if (tid + 256 * kk < nb && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -371,10 +362,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
   uint32_t taken = 0, eq_seen = 0;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int k = 0; k < (KPT > 0 ? KPT : 1); ++k) {
-    for (int kk = k; kk < (KPT > 0 ? k + 1 : chunks); ++kk) {
-      if (256 * kk >= nb) break;  // uniform
+  {  // chunks of 256 keys in block order
+    for (int kk = 0; kk < chunks; ++kk) {
       const int i = tid + 256 * kk;
       const bool valid = i < nb;
       const uint64_t mk = key_at(kk) & mask;
@@ -409,12 +398,133 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   if (tid == 0 && g == 0) a.sel_cnt[r] = K;
 }
 
+// Register-resident top-k (nb <= 256*KPT, keys of blocks tid + 256*k): the
+// same radix select and selection rule as topk_kernel, with one barrier per
+// pass and one for the whole compaction.
+//   passes      three histograms in rotation: pass p counts into hist[p%3]
+//               and clears hist[(p+1)%3], whose last readers (the scans of
+//               pass p-2) finished before the barrier of pass p-1.  After
+//               the pass's barrier every wave scans hist[p%3] itself, so the
+//               chosen digit needs no broadcast through LDS.
+//   compaction  per 256-key chunk, ballots rank each lane's key among the
+//               wave's keys above the threshold (gt) and equal to it (eq);
+//               the waves' counts of every chunk cross through LDS once.  A
+//               key with gt_before / eq_before such keys at lower block ids
+//               is taken if gt, or if eq and eq_before < need, and lands at
+//               gt_before + min(eq_before, need).
+template <bool HW, int KPT>
+__global__ __launch_bounds__(256) void topk_regs_kernel(TopkArgs a) {
+  static_assert(KPT > 0 && KPT <= 64, "keys per thread");
+  __shared__ uint32_t hist[3][256];
+  __shared__ uint32_t wcnt[KPT][4];  // per chunk and wave: gt count << 16 | eq count
+
+  const int r = HW ? blockIdx.x / a.Hkv : blockIdx.x;
+  const int g = HW ? blockIdx.x % a.Hkv : 0;
+  const ReqDev rq = a.reqs[a.batch.id[r]];
+  const int64_t row = HW ? (int64_t)r * a.Hkv + g : (int64_t)r;
+  const double* S = a.scores + row * a.stride;
+  int32_t* out = a.sel_idx + row * a.k_stride;
+  const int nb = rq.nb;
+  const int K = a.k[r] < nb ? a.k[r] : nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  uint64_t keys[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) keys[k] = score_key(S[min(tid + 256 * k, nb - 1)]);
+
+  hist[0][tid] = 0;
+  __syncthreads();
+  uint64_t prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)K;  // keys still to take from the bucket of `prefix`
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    uint32_t* h = hist[pass % 3];
+    hist[(pass + 1) % 3][tid] = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      if (tid + 256 * k < nb && (keys[k] & mask) == prefix) atomicAdd(&h[(keys[k] >> shift) & 255u], 1u);
+    __syncthreads();
+    // lane l holds digits 255-4l .. 252-4l (descending order)
+    uint32_t c[4], local = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[e] = h[255 - 4 * lane - e];
+      local += c[e];
+    }
+    uint32_t incl = local;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const uint32_t o = __shfl_up(incl, m);
+      if (lane >= m) incl += o;
+    }
+    uint32_t run = incl - local;  // keys in higher digits
+    int f_digit = -1;
+    uint32_t f_above = 0, f_count = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (run < need && need <= run + c[e]) {  // one digit of one lane: the bucket holding rank `need`
+        f_digit = 255 - 4 * lane - e;
+        f_above = run;
+        f_count = c[e];
+      }
+      run += c[e];
+    }
+    const int src = __ffsll((unsigned long long)__ballot(f_digit >= 0)) - 1;
+    const uint32_t digit = (uint32_t)__shfl(f_digit, src);
+    const uint32_t above = (uint32_t)__shfl((int)f_above, src);
+    const uint32_t count = (uint32_t)__shfl((int)f_count, src);
+    prefix |= (uint64_t)digit << shift;
+    mask |= 255ull << shift;
+    need -= above;
+    if (count == need) break;  // every key of the bucket is taken (uniform: all waves read one histogram)
+  }
+
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const bool valid = tid + 256 * k < nb;
+    const uint64_t mk = keys[k] & mask;
+    const uint64_t gt_b = __ballot(valid && mk > prefix);
+    const uint64_t eq_b = __ballot(valid && mk == prefix);
+    if (lane == 0) wcnt[k][wave] = (uint32_t)__popcll(gt_b) << 16 | (uint32_t)__popcll(eq_b);
+  }
+  __syncthreads();
+  uint32_t before = 0;  // gt << 16 | eq counts of the chunks already passed
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const bool valid = tid + 256 * k < nb;
+    const uint64_t mk = keys[k] & mask;
+    const bool gt = valid && mk > prefix, eq = valid && mk == prefix;
+    const uint64_t gt_b = __ballot(gt);
+    const uint64_t eq_b = __ballot(eq);
+    uint32_t base = before;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t cw = wcnt[k][w];
+      if (w < wave) base += cw;
+      before += cw;
+    }
+    const uint32_t gt_before = (base >> 16) + (uint32_t)__popcll(gt_b & lt_mask);
+    const uint32_t eq_before = (base & 0xffffu) + (uint32_t)__popcll(eq_b & lt_mask);
+    if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = tid + 256 * k;
+  }
+  for (int i = K + tid; i < a.k_stride; i += 256) out[i] = -1;
+  if (tid == 0 && g == 0) a.sel_cnt[r] = K;
+}
+
 template <int KPT>
 void topk_launch(const TopkArgs& a, dim3 grid, bool hw, hipStream_t s, KEv ev) {
-  if (hw)
-    KVOFF_LAUNCH(ev, (topk_kernel<true, KPT>), grid, dim3(256), 0, s, a);
-  else
-    KVOFF_LAUNCH(ev, (topk_kernel<false, KPT>), grid, dim3(256), 0, s, a);
+  if constexpr (KPT > 0) {
+    if (hw)
+      KVOFF_LAUNCH(ev, (topk_regs_kernel<true, KPT>), grid, dim3(256), 0, s, a);
+    else
+      KVOFF_LAUNCH(ev, (topk_regs_kernel<false, KPT>), grid, dim3(256), 0, s, a);
+  } else {
+    if (hw)
+      KVOFF_LAUNCH(ev, (topk_kernel<true>), grid, dim3(256), 0, s, a);
+    else
+      KVOFF_LAUNCH(ev, (topk_kernel<false>), grid, dim3(256), 0, s, a);
+  }
 }
 
 template <int NC, int MODE, bool NT>
