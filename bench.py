@@ -82,7 +82,8 @@ def parse():
                    help="time the serial order on one stream as the value instead of "
                         "kvoff_step (every gather then runs alone: clean kernel traces)")
     p.add_argument("--report", choices=["fragmentation", "admission", "groups", "mass", "decode32",
-                                        "attention-cache", "attention-heads"], default=None,
+                                        "attention-cache", "attention-heads", "select-modes"],
+                   default=None,
                    help="instead of the bench line: fragmentation = recall of the "
                         "headwise-vs-SoloHead workload with every engine; admission = the "
                         "admission policy as a control loop over the multi-layer step; groups = "
@@ -91,7 +92,8 @@ def parse():
                         "decode32 = the overlapped 32-layer decode step; attention-cache = "
                         "sparse attention with its input warm, after a 1 GiB read and after "
                         "a 1 GiB write; attention-heads = sparse attention with 4, 8 and 16 "
-                        "query heads per KV head over the same records")
+                        "query heads per KV head over the same records; select-modes = score "
+                        "and top-k kernel times of every selection mode")
     args = p.parse_args()
     if args.steps < 1 or args.warmup < 0:
         p.error("--steps must be at least 1 and --warmup at least 0")
@@ -553,6 +555,57 @@ def mass_report(args):
     print(json.dumps(res), flush=True)
 
 
+def select_modes_report(args):
+    """Score and top-k kernels of every selection mode on the Llama-3-8B-shaped
+    layer (batch 16, 32/8 heads, context 32768, top-64 per set), kernel
+    durations from start/stop events bound to each dispatch
+    (kvoff_set_kernel_timing), over 4 rotating layers so that no call finds
+    its digests in the MALL."""
+    sp = synth.spec(2)
+    reqs = synth.request_draws(sp)
+    B = len(reqs)
+    layers = list(range(4))
+    log(f"generating {len(layers)} layers of '{sp.name}' ({B} requests)")
+    case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                        layers, reqs, keep=lambda l, r: False)
+    topk = [rq.k for rq in reqs]
+    nb_tot = sum(rq.nb for rq in reqs)
+    runs = []
+    modes = [("solohead", kv.KVOFF_SOLOHEAD), ("headwise", kv.KVOFF_HEADWISE),
+             ("consensus", kv.KVOFF_CONSENSUS), ("group_consensus", kv.KVOFF_CONSENSUS_GROUP)]
+    kv.kvoff_set_consensus_lambda(case.ctx, 0.5)
+    for name, mode in modes:
+        bufs = H.make_buffers(case, mode)
+        sets = sp.Hkv if mode in (kv.KVOFF_HEADWISE, kv.KVOFF_CONSENSUS_GROUP) else 1
+
+        def select(i):
+            l = layers[i % len(layers)]
+            kv.kvoff_select(case.ctx, l, case.rids, case.q[l], case.digest[l], case.nb_max, topk,
+                            mode, bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+
+        for i in range(args.warmup):
+            select(i)
+        kv.kvoff_set_kernel_timing(case.ctx, True)
+        for i in range(args.steps):
+            select(i)
+        t = kv.kvoff_get_kernel_times(case.ctx)
+        kv.kvoff_set_kernel_timing(case.ctx, False)
+        score_bytes = nb_tot * sp.Hkv * sp.d * 4 + B * sp.Hq * sp.d * sp.es + nb_tot * sets * 8
+        gbps = score_bytes / (t["score_ms"] * 1e-3) / 1e9
+        res = {"mode": name, "score_us": round(t["score_ms"] * 1e3, 2),
+               "topk_us": round(t["topk_ms"] * 1e3, 2), "score_bytes": score_bytes,
+               "score_hbm_gbps": round(gbps, 1), "score_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+               "calls": t["select_calls"]}
+        log(str(res))
+        runs.append(res)
+    res = {"workload": f"{sp.name}: batch {B}, {sp.Hq}/{sp.Hkv} heads, context {reqs[0].ctx}, "
+                       f"block {sp.bs}, top-{reqs[0].k} per set, {len(layers)} rotating layers",
+           "how": "kernel durations from start/stop events bound to each dispatch "
+                  "(kvoff_set_kernel_timing), consensus lambda 0.5", "runs": runs}
+    H.destroy(case)
+    print(json.dumps(res), flush=True)
+
+
 def attention_cache_report(args):
     """Sparse attention on the Llama-3-8B-shaped and the variable-recall
     layers, three ways: warm (calls back to back; 128 MiB of records stay in
@@ -773,6 +826,8 @@ def main():
         return attention_cache_report(args)
     if args.report == "attention-heads":
         return attention_heads_report(args)
+    if args.report == "select-modes":
+        return select_modes_report(args)
     sp = synth.spec(args.config if args.config else args.workload, L=args.layers)
     reqs = synth.request_draws(sp)
     B = len(reqs)
