@@ -87,13 +87,22 @@ __device__ __forceinline__ double sum32(double v) {
   return v + __shfl_xor(v, 16);
 }
 
+// x from lane (lane ^ m), m < 32 a constant once loops are unrolled: DPP
+// quad permutes for 1 and 2, a shuffle otherwise
+__device__ __forceinline__ double xor_move(double x, int m) {
+  if (m == 1) return dpp_move<0xB1>(x);  // quad_perm [1,0,3,2]
+  if (m == 2) return dpp_move<0x4E>(x);  // quad_perm [2,3,0,1]
+  return __shfl_xor(x, m);
+}
+
 template <bool BF16>
 __device__ __forceinline__ double widen_t(uint16_t h) {
   if constexpr (BF16) return (double)__uint_as_float((uint32_t)h << 16);
   else return (double)__builtin_bit_cast(_Float16, h);
 }
 
-template <int NC, int MODE, bool BF16, bool NT>
+// GG: the group size G as a constant (consensus within GQA groups only)
+template <int NC, int MODE, bool BF16, bool NT, int GG>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ double u_s[NC * 256];
   extern __shared__ uint4 q_s[];  // the request's q rows, Hq * 16 chunks of 16 bytes
@@ -168,40 +177,63 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     // consensus within each GQA group: per query head h of group g,
     // s_h = <q_h, D[b][g]>; S_g = max_h s_h + lambda * mean_h s_h.  Lane
     // holds dims idx..idx+3 of KV head idx/128 in chunk c (chunk c covers
-    // heads 2c and 2c+1); dims past the row contribute nothing.
+    // heads 2c and 2c+1 in lanes 0-31 and 32-63); dims past the row
+    // contribute nothing.  The GG per-head partials of a lane are summed over
+    // its 32 lanes by a reduce-scatter: at step st (lane bit st, st < log2
+    // GG) a lane keeps half of its values and adds the partner lane's copies
+    // of them, so after log2 GG steps it holds one head's sum over GG lanes,
+    // and the remaining steps of the 32-lane butterfly complete it.  The
+    // group's head sums then sit in the lanes that differ in bits 0 .. log2
+    // GG - 1, where a butterfly takes their max and their sum.  Additions
+    // commute, so every lane ends with the same bits.  (Sharing each q
+    // slice's widening between the wave's two blocks needs 116 VGPRs instead
+    // of 72 at G = 4 and was slower: 28.3 against 23.1 us.)
+    static_assert(GG >= 1 && GG <= 16 && (GG & (GG - 1)) == 0, "group size");
+    constexpr int LG = GG >= 16 ? 4 : GG >= 8 ? 3 : GG >= 4 ? 2 : GG >= 2 ? 1 : 0;
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_s);
 #pragma unroll
     for (int k = 0; k < SCORE_BPW; ++k) {
       const int64_t b = bw + k;
-      double mx[NC], sm[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        mx[c] = -INFINITY;
-        sm[c] = 0.0;
-      }
-      for (int i = 0; i < a.G; ++i) {
+        const int idx = c * 256 + lane * 4;
+        const int g = min(idx, F - 4) / kHeadDim, j0 = idx % kHeadDim;
+        double p[GG];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int idx = c * 256 + lane * 4;
+        for (int i = 0; i < GG; ++i) {
           double acc = 0.0;
           if (idx < F) {
-            const int g = idx / kHeadDim, j0 = idx % kHeadDim;
-            const uint2 w = *reinterpret_cast<const uint2*>(q16 + (g * a.G + i) * kHeadDim + j0);
+            const uint2 w = *reinterpret_cast<const uint2*>(q16 + (g * GG + i) * kHeadDim + j0);
             acc = fma(widen_t<BF16>((uint16_t)(w.x & 0xffffu)), (double)v[k][c].x, acc);
             acc = fma(widen_t<BF16>((uint16_t)(w.x >> 16)), (double)v[k][c].y, acc);
             acc = fma(widen_t<BF16>((uint16_t)(w.y & 0xffffu)), (double)v[k][c].z, acc);
             acc = fma(widen_t<BF16>((uint16_t)(w.y >> 16)), (double)v[k][c].w, acc);
           }
-          acc = sum32(acc);
-          mx[c] = fmax(mx[c], acc);
-          sm[c] += acc;
+          p[i] = acc;
         }
-      }
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int g = (c * 256 + (lane & 32) * 4) / kHeadDim;
-        if ((lane & 31) == 0 && b < rq.nb && g < a.Hkv)
-          a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = mx[c] + a.lambda * (sm[c] / (double)a.G);
+        for (int st = 0; st < LG; ++st) {
+          const int half = GG >> (st + 1);
+          const bool up = (lane >> st) & 1;
+#pragma unroll
+          for (int j = 0; j < half; ++j) {
+            const double keep = up ? p[j + half] : p[j];
+            const double send = up ? p[j] : p[j + half];
+            p[j] = keep + xor_move(send, 1 << st);
+          }
+        }
+        double sum = p[0];
+#pragma unroll
+        for (int st = LG; st < 5; ++st) sum += xor_move(sum, 1 << st);
+        double mx = sum, sm = sum;
+#pragma unroll
+        for (int st = 0; st < LG; ++st) {
+          mx = fmax(mx, xor_move(mx, 1 << st));
+          sm += xor_move(sm, 1 << st);
+        }
+        const int gw = (c * 256 + (lane & 32) * 4) / kHeadDim;  // the half's KV head
+        if ((lane & 31) == 0 && b < rq.nb && gw < a.Hkv)
+          a.scores[((int64_t)r * a.Hkv + gw) * a.stride + b] = mx + a.lambda * (sm / (double)GG);
       }
     }
     return;
@@ -527,14 +559,29 @@ void topk_launch(const TopkArgs& a, dim3 grid, bool hw, hipStream_t s, KEv ev) {
   }
 }
 
-template <int NC, int MODE, bool NT>
-void score_launch_b(const ScoreArgs& a, int64_t max_nb, hipStream_t s, KEv ev) {
+template <int NC, int MODE, bool NT, int GG>
+void score_launch_g(const ScoreArgs& a, int64_t max_nb, hipStream_t s, KEv ev) {
   const uint32_t lds = (uint32_t)std::max<size_t>((size_t)a.Hq * kHeadDim * 2, 4 * 256 * 16);  // staged q rows
   const dim3 grid((unsigned)((max_nb + SCORE_WG_BLOCKS - 1) / SCORE_WG_BLOCKS), (unsigned)a.batch.n);
   if (a.bf16)
-    KVOFF_LAUNCH(ev, (score_kernel<NC, MODE, true, NT>), grid, dim3(256), lds, s, a);
+    KVOFF_LAUNCH(ev, (score_kernel<NC, MODE, true, NT, GG>), grid, dim3(256), lds, s, a);
   else
-    KVOFF_LAUNCH(ev, (score_kernel<NC, MODE, false, NT>), grid, dim3(256), lds, s, a);
+    KVOFF_LAUNCH(ev, (score_kernel<NC, MODE, false, NT, GG>), grid, dim3(256), lds, s, a);
+}
+
+template <int NC, int MODE, bool NT>
+void score_launch_b(const ScoreArgs& a, int64_t max_nb, hipStream_t s, KEv ev) {
+  if constexpr (MODE == MODE_GROUP) {
+    switch (a.G) {
+      case 1: return score_launch_g<NC, MODE, NT, 1>(a, max_nb, s, ev);
+      case 2: return score_launch_g<NC, MODE, NT, 2>(a, max_nb, s, ev);
+      case 4: return score_launch_g<NC, MODE, NT, 4>(a, max_nb, s, ev);
+      case 8: return score_launch_g<NC, MODE, NT, 8>(a, max_nb, s, ev);
+      default: return score_launch_g<NC, MODE, NT, 16>(a, max_nb, s, ev);
+    }
+  } else {
+    score_launch_g<NC, MODE, NT, 0>(a, max_nb, s, ev);
+  }
 }
 
 template <int NC, int MODE>
