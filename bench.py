@@ -40,7 +40,7 @@ METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM 
 # workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
 # and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
 # the recall source it was taken with: reported as null once that changes.
-GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65610.98, "write_kib": 131076.03,
+GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65604.9, "write_kib": 131076.2,
               "fetch_scale": 1.9999, "write_scale": 1.0000,
               "recall_src_sha256": "e4f84d2d465c8c7cb8540f214126917d14080726170791c7d2ae292955dcde73"}
 
