@@ -262,8 +262,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       if (lane == 0 && b < rq.nb) a.scores[(int64_t)r * a.stride + b] = acc;
     } else {
       // per-KV-head sums: a KV head's 128 dims are 32 consecutive lanes of
-      // one chunk, so chunk c holds heads 2c (lanes 0-31) and 2c+1 (32-63)
-      double sg[NC];
+      // one chunk, so chunk c holds heads 2c (lanes 0-31) and 2c+1 (32-63).
+      // The NC chunk partials are summed over their 32 lanes by a
+      // reduce-scatter, as in the GQA-group mode: after log2 NC halving steps
+      // lane bits 0 .. log2 NC - 1 name the lane's chunk, and the rest of
+      // the butterfly completes its sum.
+      constexpr int LN = NC >= 8 ? 3 : NC >= 4 ? 2 : NC >= 2 ? 1 : 0;
+      double p[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         double acc = 0.0;
@@ -271,35 +276,39 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         acc = fma(u[c][1], (double)v[k][c].y, acc);
         acc = fma(u[c][2], (double)v[k][c].z, acc);
         acc = fma(u[c][3], (double)v[k][c].w, acc);
-        sg[c] = sum32(acc);
+        p[c] = acc;
       }
+      int c = 0;  // the chunk whose sum this lane ends with
+#pragma unroll
+      for (int st = 0; st < LN; ++st) {
+        const int half = NC >> (st + 1);
+        const bool up = (lane >> st) & 1;
+        c += up ? half : 0;
+#pragma unroll
+        for (int j = 0; j < half; ++j) {
+          const double keep = up ? p[j + half] : p[j];
+          const double send = up ? p[j] : p[j + half];
+          p[j] = keep + xor_move(send, 1 << st);
+        }
+      }
+      double sg = p[0];
+#pragma unroll
+      for (int st = LN; st < 5; ++st) sg += xor_move(sg, 1 << st);
+      const int g = 2 * c + (lane >> 5);  // this lane's KV head
       if constexpr (MODE == MODE_HEADWISE) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int g = (c * 256 + lane * 4) / kHeadDim;
-          if ((lane & 31) == 0 && b < rq.nb && g < a.Hkv)
-            a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = sg[c];
-        }
+        if ((lane & 31) < NC && b < rq.nb && g < a.Hkv)
+          a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = sg;
       } else {
-        // consensus: S = max_g S_g + lambda * mean_g S_g, heads in order
-        double hi[NC];
+        // consensus: S = max_g S_g + lambda * mean_g S_g over the KV heads
+        double mx = g < a.Hkv ? sg : -INFINITY, sm = g < a.Hkv ? sg : 0.0;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) hi[c] = __shfl(sg[c], 32);
-        if (lane == 0 && b < rq.nb) {
-          double mx = sg[0], sum = 0.0;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            if (2 * c < a.Hkv) {
-              mx = fmax(mx, sg[c]);
-              sum += sg[c];
-            }
-            if (2 * c + 1 < a.Hkv) {
-              mx = fmax(mx, hi[c]);
-              sum += hi[c];
-            }
-          }
-          a.scores[(int64_t)r * a.stride + b] = mx + a.lambda * (sum / (double)a.Hkv);
+        for (int st = 0; st < LN; ++st) {
+          mx = fmax(mx, xor_move(mx, 1 << st));
+          sm += xor_move(sm, 1 << st);
         }
+        mx = fmax(mx, __shfl_xor(mx, 32));
+        sm += __shfl_xor(sm, 32);
+        if (lane == 0 && b < rq.nb) a.scores[(int64_t)r * a.stride + b] = mx + a.lambda * (sm / (double)a.Hkv);
       }
     }
   }
