@@ -547,7 +547,8 @@ __global__ __launch_bounds__(256) void topk_regs_kernel(TopkArgs a) {
     }
     const uint32_t gt_before = (base >> 16) + (uint32_t)__popcll(gt_b & lt_mask);
     const uint32_t eq_before = (base & 0xffffu) + (uint32_t)__popcll(eq_b & lt_mask);
-    if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = tid + 256 * k;
+    const uint32_t pos = gt_before + min(eq_before, need);
+    if ((gt || (eq && eq_before < need)) && pos < (uint32_t)K) out[pos] = tid + 256 * k;  // pos < K by construction
   }
   for (int i = K + tid; i < a.k_stride; i += 256) out[i] = -1;
   if (tid == 0 && g == 0) a.sel_cnt[r] = K;
