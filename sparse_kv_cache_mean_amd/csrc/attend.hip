@@ -139,8 +139,12 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// G = 8 with both contractions on the matrix cores fits 3 waves per SIMD
+// when asked (145 VGPRs, no spills; left to itself the compiler takes 176 +
+// 32 accumulation registers, 2 waves)
 template <int G, int BS, bool BF16, bool MFMA>
-__global__ __launch_bounds__(256) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MFMA && BS == 32 && G == 8 ? 3 : 1)))
+void attend_kernel(AttendArgs a) {
   static_assert(MFMA || G <= 8, "the VALU QK keeps every head's query slice in registers");
   static_assert(G <= 16, "one MFMA tile holds the group's heads");
   constexpr int D = kHeadDim;
