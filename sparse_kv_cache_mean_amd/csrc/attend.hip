@@ -139,11 +139,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// G = 8 with both contractions on the matrix cores fits 3 waves per SIMD
-// when asked (145 VGPRs, no spills; left to itself the compiler takes 176 +
-// 32 accumulation registers, 2 waves)
+// G >= 8 with both contractions on the matrix cores fits 3 waves per SIMD
+// when asked (G = 8: 145 VGPRs, no spills; left to itself the compiler takes
+// 176 + 32 accumulation registers, 2 waves)
 template <int G, int BS, bool BF16, bool MFMA>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MFMA && BS == 32 && G == 8 ? 3 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MFMA && BS == 32 && G >= 8 ? 3 : 1)))
 void attend_kernel(AttendArgs a) {
   static_assert(MFMA || G <= 8, "the VALU QK keeps every head's query slice in registers");
   static_assert(G <= 16, "one MFMA tile holds the group's heads");
@@ -161,8 +161,16 @@ void attend_kernel(AttendArgs a) {
   __shared__ float p_s[ATT_WAVES][PVM ? 1 : BS][G];
   __shared__ float alpha_s[ATT_WAVES][PVM ? 16 : G];
   __shared__ float wm[ATT_WAVES][G], wl[ATT_WAVES][G];
-  __shared__ float wo[ATT_WAVES][G][D];
-  __shared__ uint16_t v_s[ATT_WAVES][PVM ? BS * VS : 1];
+  // the waves' o partials for the final merge; with P V on the matrix cores
+  // each wave's share lives in its own V tile (8,448 bytes, at most 8,192
+  // needed), which that wave no longer reads once its block loop is done
+  __shared__ float wo_s[ATT_WAVES][PVM ? 1 : G][D];
+  __shared__ __align__(16) uint16_t v_s[ATT_WAVES][PVM ? BS * VS : 1];
+  static_assert(!PVM || G * D * sizeof(float) <= BS * VS * sizeof(uint16_t), "o partials fit the V tile");
+  auto wo = [&](int w) -> float* {
+    if constexpr (PVM) return reinterpret_cast<float*>(&v_s[w][0]);
+    else return &wo_s[w][0][0];
+  };
 
   const int s = blockIdx.x % a.S;
   const int rg = blockIdx.x / a.S;
@@ -426,7 +434,7 @@ void attend_kernel(AttendArgs a) {
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (quad * 4 + i < G) wo[wave][quad * 4 + i][c * 16 + col] = oc[c][i] * osc;
+        if (quad * 4 + i < G) wo(wave)[(quad * 4 + i) * D + c * 16 + col] = oc[c][i] * osc;
     if (quad == 0 && col < G) {
       wm[wave][col] = m_run;
       wl[wave][col] = l_run;
@@ -444,7 +452,7 @@ void attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wo[wave][h][col * 8 + e] = o[h][e];
+        for (int e = 0; e < 8; ++e) wo(wave)[h * D + col * 8 + e] = o[h][e];
       if constexpr (MFMA) {
         if (col < G) {
           wm[wave][col] = m_run;
@@ -472,7 +480,7 @@ void attend_kernel(AttendArgs a) {
     for (int w = 0; w < ATT_WAVES; ++w) {
       const float f = wm[w][h] == -INFINITY ? 0.f : exp2f(wm[w][h] - M);
       L = fmaf(wl[w][h], f, L);
-      O = fmaf(wo[w][h][j], f, O);
+      O = fmaf(wo(w)[h * D + j], f, O);
     }
     float* P = a.part + (((int64_t)r * a.Hq + (int64_t)g * G + h) * a.S + s) * PART;
     if (j == 0) {
