@@ -328,6 +328,46 @@ def test_degenerate_sizes():
         H.destroy(c)
 
 
+# Exact score ties across the top-k boundary.  Every key of block b of
+# request r is the constant c = (7b + r) mod 3 (the last request: 0
+# everywhere) and the queries are positive, so blocks with one constant get
+# bit-identical scores on either side, ordered by the constant; the boundary
+# falls inside a tie group, which the selection must cut at the lower block
+# ids.  The three cases take the register top-k with 4 and 16 keys per thread
+# and the streaming top-k past 16,384 blocks.
+TIE_CASES = [
+    dict(wl=2, B=3, ctx=8192, k=100),                        # bf16, 32-token blocks, 256 blocks
+    dict(wl=2, B=3, ctx=65536, k=900),                       # 2,048 blocks
+    dict(wl=1, B=2, ctx=300000, k=300),                      # fp16, 16-token blocks, 18,750 blocks
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=["256-blocks", "2048-blocks", "18750-blocks"])
+def test_topk_exact_ties_take_the_lower_block_ids(case):
+    args = dict(case)
+    s = synth.spec(args.pop("wl"), headwise=True, **args)
+    H.log(f"[ties] {s.name} ctx {s.ctx} k {s.k}")
+    one, two = (0x3F80, 0x4000) if s.dtype == synth.BF16 else (0x3C00, 0x4000)
+    reqs = synth.request_draws(s)
+    sl = {}
+    for r, rq in enumerate(reqs):
+        lr = synth.gen_layer_request(s, 0, r, rq)
+        lr.q &= np.uint16(0x7FFF)
+        for b in range(rq.nb):
+            c = 0 if r == len(reqs) - 1 else (7 * b + r) % 3
+            lr.K[b * s.bs:(b + 1) * s.bs] = (0, one, two)[c]
+        sl[(0, r)] = workloads.condition(s, lr, enforce=False)
+        assert sl[(0, r)].gap == 0.0  # the boundary is a tie in every ranking
+    c = H.build_case(s, {k: v.lr for k, v in sl.items()}, [0], reqs)
+    try:
+        for mode in (kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE):
+            _full_check(c, sl, 0, mode, kv.KVOFF_ENGINE_ZEROCOPY)
+        zero = sl[(0, len(reqs) - 1)]
+        assert zero.sel.tolist() == list(range(zero.K))
+    finally:
+        H.destroy(c)
+
+
 # several layers: overlapped kvoff_step must equal the serial order bit for bit
 MULTI = synth.spec(3, B=2, L=4, ctx=3000, k=20, hot=8)
 
