@@ -428,7 +428,9 @@ void attend_kernel(AttendArgs a) {
   }
 
   if constexpr (PVM) {
-    // the MFMA accumulators already sum every token of the wave
+    // the MFMA accumulators already sum every token of the wave; the o
+    // partials overwrite this wave's V tile, so its last reads go first
+    wave_sync_lds();
     const float osc = BF16 ? 1.f : 1.f / 32768.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
