@@ -647,7 +647,7 @@ def attention_cache_report(args):
                     before(i)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[0], case.pool, bufs.table,
+                kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[0], case.pool, case.n_slots, bufs.table,
                                        bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale, bufs.out,
                                        bufs.ws)
                 e1.record()
@@ -694,7 +694,7 @@ def attention_heads_report(args):
         for _ in range(20):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[0], case.pool, bufs.table,
+            kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[0], case.pool, case.n_slots, bufs.table,
                                    bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale, bufs.out, bufs.ws)
             e1.record()
             evs.append((e0, e1))
@@ -870,7 +870,7 @@ def main():
                         engine, stream=stream)
         if evs:
             evs[2].record(stream)
-        kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[l], case.pool, bufs.table,
+        kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[l], case.pool, case.n_slots, bufs.table,
                                bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale, bufs.out,
                                bufs.ws, stream=stream)
         if evs:

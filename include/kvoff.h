@@ -95,8 +95,10 @@ enum {
      writes the HBM slots; the plan stays on the GPU, no host round trip */
   KVOFF_ENGINE_ZEROCOPY = 0,
   /* the selection is copied to the host, which issues one hipMemcpyAsync per
-     coalesced run (per (block, KV head) slice in headwise mode) on the
-     stream; synchronises that stream first */
+     coalesced run (per (block, KV head) slice in headwise mode), round robin
+     over the call's stream and up to three copy streams the context owns
+     (created on first use, non-blocking, default priority); the call's
+     stream then waits for all of them.  Synchronises that stream first */
   KVOFF_ENGINE_DMA = 1,
   /* the guide's three-phase engine ("The Gather-Scatter I/O Engine"): host
      worker threads gather the selected records into a pinned staging
@@ -228,6 +230,7 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
 
 /* Recall the selected blocks of one layer into the HBM slot pool.
  *   slot_pool_dev [n_slots] records of kvoff_record_bytes() each, in HBM
+ *                 (the pool holds n_slots records; owned by the caller)
  *   recall_base_slot  first slot of the recall region: the record of rank i
  *                 of request r goes to slot recall_base_slot + r*k_stride + i
  *                 (headwise: KV head g's slice of that slot), so consecutive
@@ -235,14 +238,22 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
  *                 one contiguous copy on both sides
  *   pool_hit_dev  nullable [n_req][pool_stride] uint8: 1 where block b of
  *                 request r is already resident in the pool at slot
- *                 pool_slot_dev[r*pool_stride + b]; resident blocks are not moved
+ *                 pool_slot_dev[r*pool_stride + b]; resident blocks are not
+ *                 moved.  A hit whose slot lies outside [0, n_slots) (for
+ *                 instance -1) gets the table entry -1, so kvoff_sparse_decode
+ *                 never reads it, and is not counted in the stats.  The DMA
+ *                 and staged engines, which read the maps on the host, then
+ *                 return KVOFF_ESTATE once the call's work is enqueued; the
+ *                 zero-copy engine counts such hits on the device and the next
+ *                 call on the context that fills stats (this one, or a later
+ *                 kvoff_recall or kvoff_step) returns KVOFF_ESTATE for them
  *   block_table_dev out: SoloHead [n_req][k_stride] slot of each rank;
  *                 headwise [n_req][Hkv][k_stride] slice index (slot*Hkv + g);
  *                 unused entries -1
  *   engine        KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA or KVOFF_ENGINE_STAGED
  *   stats         nullable; when given, filled after synchronising the stream
  * Errors: EINVAL, ERANGE (recall region past n_slots), ESTATE (layer of a
- * request not offloaded), EHIP. */
+ * request not offloaded, or pool hits outside the pool as above), EHIP. */
 int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* req_ids,
                  int32_t mode, const int32_t* sel_idx_dev, const int32_t* sel_cnt_dev,
                  int32_t k_stride, const uint8_t* pool_hit_dev, const int32_t* pool_slot_dev,
@@ -254,12 +265,16 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
 
 /* Sparse GQA decode attention over the recalled blocks.
  *   q_dev         [n_req][Hq][d]
+ *   slot_pool_dev, n_slots: the slot pool kvoff_recall filled, n_slots
+ *                 records of kvoff_record_bytes() (1 <= n_slots and
+ *                 n_slots * Hkv <= INT32_MAX)
  *   block_table_dev, sel_idx_dev, sel_cnt_dev, k_stride: as produced by
  *                 kvoff_recall / kvoff_select (sel_idx gives each entry's
  *                 block id, so a request's partial last block is masked).
- *                 Block ids outside a request and negative table entries
- *                 are skipped; a table entry is otherwise trusted to lie in
- *                 slot_pool_dev (the pool's size is not passed here).
+ *                 Entries that are not a block of the request or of the pool
+ *                 are skipped: a block id outside the request, a negative
+ *                 table entry, or one at or past n_slots (headwise: slice
+ *                 index at or past n_slots * Hkv).
  *   scale         logit scale (1/sqrt(d) for standard attention)
  *   out_dev       out: [n_req][Hq][d] fp32
  *   ws_dev        scratch of at least kvoff_workspace_size(ctx,
@@ -267,7 +282,7 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
  * Head h reads KV head floor(h/G).  Errors: EINVAL, ERANGE (ws too small),
  * ESTATE, EHIP. */
 int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, int32_t mode,
-                        const void* q_dev, const void* slot_pool_dev,
+                        const void* q_dev, const void* slot_pool_dev, int64_t n_slots,
                         const int32_t* block_table_dev, const int32_t* sel_idx_dev,
                         const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
                         float* out_dev, void* ws_dev, size_t ws_bytes, void* stream);
@@ -290,6 +305,12 @@ size_t kvoff_workspace_size(const kvoff_ctx* ctx, int32_t call, int32_t n_req,
  * Offloading", and of its layer-wise scheduling).  With copy_stream equal to
  * compute_stream the layers run serially.  Outputs equal a serial run bit
  * for bit.
+ * Errors are found before any work is enqueued (EINVAL, ERANGE, ESTATE for
+ * an unregistered request or a layer not offloaded; overlapped layers,
+ * L > 1 with copy_stream != compute_stream, need recall regions of n_req *
+ * k_stride slots that share no slot, else EINVAL), except the pool-slot
+ * report of kvoff_recall: with stats, a step whose pool hits named slots
+ * outside the pool still runs every layer and then returns KVOFF_ESTATE.
  * A call can be captured into a HIP graph on its compute stream (stream
  * capture; the copy streams join it through the call's own events) when the
  * engine is KVOFF_ENGINE_ZEROCOPY and stats and timing are NULL: the

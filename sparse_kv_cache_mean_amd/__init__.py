@@ -138,8 +138,8 @@ def lib() -> ctypes.CDLL:
     L.kvoff_select.argtypes = [_vp, i32, i32, _vp, _vp, _vp, i64, _vp, i32, _vp, _vp, _vp, i32, _vp]
     L.kvoff_recall.argtypes = [_vp, i32, i32, _vp, i32, _vp, _vp, i32, _vp, _vp, i64, _vp, i64,
                                i64, _vp, i32, _vp, _vp]
-    L.kvoff_sparse_decode.argtypes = [_vp, i32, _vp, i32, _vp, _vp, _vp, _vp, _vp, i32, f32, _vp,
-                                      _vp, sz, _vp]
+    L.kvoff_sparse_decode.argtypes = [_vp, i32, _vp, i32, _vp, _vp, i64, _vp, _vp, _vp, i32, f32,
+                                      _vp, _vp, sz, _vp]
     L.kvoff_workspace_size.argtypes = [_vp, i32, i32, i32, i32]
     L.kvoff_workspace_size.restype = sz
     L.kvoff_step.argtypes = [_vp, P(kvoff_step_args)]
@@ -280,13 +280,13 @@ def kvoff_workspace_size(ctx: int, call: int, n_req: int, k_stride: int, mode: i
     return int(lib().kvoff_workspace_size(ctx, call, n_req, k_stride, mode))
 
 
-def kvoff_sparse_decode(ctx: int, req_ids: Sequence[int], mode: int, q, slot_pool, block_table,
-                        sel_idx, sel_cnt, k_stride: int, scale: float, out, ws,
+def kvoff_sparse_decode(ctx: int, req_ids: Sequence[int], mode: int, q, slot_pool, n_slots: int,
+                        block_table, sel_idx, sel_cnt, k_stride: int, scale: float, out, ws,
                         stream=None) -> None:
     ids = _i32_array(req_ids)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().kvoff_sparse_decode(ctx, len(req_ids), ids, mode, _ptr(q), _ptr(slot_pool),
-                                     _ptr(block_table), _ptr(sel_idx), _ptr(sel_cnt), k_stride,
+                                     n_slots, _ptr(block_table), _ptr(sel_idx), _ptr(sel_cnt), k_stride,
                                      scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 

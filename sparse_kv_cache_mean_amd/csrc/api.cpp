@@ -181,6 +181,10 @@ int kvoff_destroy(kvoff_ctx* ctx) {
     for (hipEvent_t e : ctx->ev_group) (void)hipEventDestroy(e);
     for (hipEvent_t e : ctx->ev_timing) (void)hipEventDestroy(e);
     if (ctx->copy2) (void)hipStreamDestroy(ctx->copy2);
+    for (int k = 0; k < kDmaSideStreams; ++k) {
+      if (ctx->dma_stream[k]) (void)hipStreamDestroy(ctx->dma_stream[k]);
+      if (ctx->dma_done[k]) (void)hipEventDestroy(ctx->dma_done[k]);
+    }
     for (hipEvent_t e : ctx->kt_ev)
       if (e) (void)hipEventDestroy(e);
     if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
@@ -338,21 +342,30 @@ static int read_counters(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a,
   stats->transfers = (int64_t)c[3];
   stats->bytes = (int64_t)c[2] * item;
   (void)b;
+  if (c[kBadSlots]) {
+    // reported once: cleared for the calls that follow
+    int st = launch_zero_counters(ctx, true, s);
+    if (st) return st;
+    return fail(KVOFF_ESTATE,
+                "%llu pool hits (this call and earlier ones without stats) named a slot outside "
+                "the pool: table entries -1",
+                c[kBadSlots]);
+  }
   return KVOFF_OK;
 }
 
-static int recall_impl(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, int64_t n_slots,
-                       int32_t engine, kvoff_stats* stats, hipStream_t s) {
+static int recall_impl(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, int32_t engine,
+                       kvoff_stats* stats, hipStream_t s) {
   if (a.recall_base_slot < 0 ||
-      a.recall_base_slot + (int64_t)b.n * a.k_stride > n_slots)
+      a.recall_base_slot + (int64_t)b.n * a.k_stride > a.n_slots)
     return fail(KVOFF_ERANGE, "recall region [%lld, %lld) exceeds the pool's %lld slots",
                 (long long)a.recall_base_slot,
-                (long long)(a.recall_base_slot + (int64_t)b.n * a.k_stride), (long long)n_slots);
+                (long long)(a.recall_base_slot + (int64_t)b.n * a.k_stride), (long long)a.n_slots);
   if (engine == KVOFF_ENGINE_DMA) return recall_dma(ctx, b, a, stats, s);
   if (engine == KVOFF_ENGINE_STAGED) return recall_staged(ctx, b, a, stats, s);
   if (engine != KVOFF_ENGINE_ZEROCOPY) return fail(KVOFF_EINVAL, "engine %d", engine);
   int st;
-  if (stats && (st = launch_zero_counters(ctx, s))) return st;
+  if (stats && (st = launch_zero_counters(ctx, false, s))) return st;
   if ((st = launch_gather(ctx, b, a, stats != nullptr, s))) return st;
   if (stats) return read_counters(ctx, b, a, stats, s);
   return KVOFF_OK;
@@ -385,9 +398,10 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
           return fail(KVOFF_EINVAL, "pool_stride %lld < nb of request %d", (long long)pool_stride, i);
     }
     KVOFF_HIP(hipSetDevice(ctx->device));
-    RecallArgs a{layer, mode, sel_idx_dev, sel_cnt_dev, k_stride, pool_hit_dev, pool_slot_dev,
-                 pool_stride, (uint8_t*)slot_pool_dev, recall_base_slot, block_table_dev};
-    return recall_impl(ctx, b, a, n_slots, engine, stats, (hipStream_t)stream);
+    RecallArgs a{layer,       mode,         sel_idx_dev, sel_cnt_dev,
+                 k_stride,    pool_hit_dev, pool_slot_dev, pool_stride,
+                 (uint8_t*)slot_pool_dev, n_slots, recall_base_slot, block_table_dev};
+    return recall_impl(ctx, b, a, engine, stats, (hipStream_t)stream);
   });
 }
 
@@ -401,7 +415,7 @@ size_t kvoff_workspace_size(const kvoff_ctx* ctx, int32_t call, int32_t n_req, i
 }
 
 int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, int32_t mode,
-                        const void* q_dev, const void* slot_pool_dev,
+                        const void* q_dev, const void* slot_pool_dev, int64_t n_slots,
                         const int32_t* block_table_dev, const int32_t* sel_idx_dev,
                         const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
                         float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
@@ -416,11 +430,14 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
     mode = layout_of(mode);  // consensus modes use the layout of their scope
     if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
     if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
+    if (n_slots < 1 || n_slots > INT32_MAX / ctx->cfg.num_kv_heads)
+      return fail(KVOFF_EINVAL, "n_slots %lld outside [1, %d]", (long long)n_slots,
+                  INT32_MAX / ctx->cfg.num_kv_heads);
     size_t need = attend_ws_bytes(ctx, n_req, k_stride);
     if (need > 0 && (!ws_dev || ws_bytes < need))
       return fail(KVOFF_ERANGE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
     KVOFF_HIP(hipSetDevice(ctx->device));
-    st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, block_table_dev, sel_idx_dev,
+    st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, n_slots, block_table_dev, sel_idx_dev,
                        sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
     if (st) return st;
     if ((st = kernel_timing_advance(ctx, KT_ATTEND))) return st;

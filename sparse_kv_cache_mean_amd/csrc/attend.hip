@@ -70,6 +70,7 @@ struct AttendArgs {
   const int32_t* sel_cnt;
   float* part;
   int64_t slice_bytes;
+  int64_t n_slices;  // slices the pool holds (n_slots * Hkv); entries at or past it are skipped
   int32_t k_stride, S, bpw, Hq, Hkv, hw;
   float scale_log2;
 };
@@ -420,7 +421,8 @@ void attend_kernel(AttendArgs a) {
       const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
       const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
       const int n_valid = (int)min<int64_t>(BS, (int64_t)rq.n_tokens - (int64_t)blk * BS);
-      if (ent < 0 || blk < 0 || n_valid <= 0) continue;  // not a valid entry: nothing to read
+      // not a valid entry (unused, or outside the request or the pool): nothing to read
+      if (ent < 0 || slice >= a.n_slices || blk < 0 || n_valid <= 0) continue;
       uint4 kf[TILES][4], vf[BS / 4];
       load_tiles(Kp, kf, vf);
       process(kf, vf, n_valid);
@@ -585,7 +587,7 @@ size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride) {
 }
 
 int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,
-                  const void* pool, const int32_t* table, const int32_t* sel_idx,
+                  const void* pool, int64_t n_slots, const int32_t* table, const int32_t* sel_idx,
                   const int32_t* sel_cnt, int32_t k_stride, float scale, float* out, void* ws,
                   hipStream_t stream) {
   AttendArgs a;
@@ -598,6 +600,7 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   a.sel_cnt = sel_cnt;
   a.part = (float*)ws;
   a.slice_bytes = ctx->slice_bytes;
+  a.n_slices = n_slots * ctx->cfg.num_kv_heads;
   a.k_stride = k_stride;
   a.bpw = attend_bpw(k_stride, ctx->G);
   a.S = attend_splits(k_stride, ctx->G);

@@ -18,6 +18,14 @@ namespace kvoff {
 
 constexpr int kHeadDim = 128;
 
+// device statistics counters of the context (d_counters[8]): 0..3 the
+// per-call recall statistics (selected, pool hits, items, transfers), and
+// the sticky count of pool hits whose slot lay outside the pool
+constexpr int kBadSlots = 4;
+
+// copy streams the DMA engine owns beside the caller's
+constexpr int kDmaSideStreams = 3;
+
 // Per-request entry of the device request table.  The record of
 // (layer, request, block) sits at store + (rec_base + layer*nb + block) * rec_bytes.
 struct ReqDev {
@@ -81,6 +89,8 @@ struct kvoff_ctx {
   std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
   hipStream_t copy2 = nullptr;              // kvoff_step's own second copy stream (lazy)
+  hipStream_t dma_stream[kvoff::kDmaSideStreams] = {};  // DMA engine's copy streams (lazy)
+  hipEvent_t dma_done[kvoff::kDmaSideStreams] = {};     // behind each one's last copy
   bool ev_stage_pending = false;
   // per-kernel timing (kvoff_set_kernel_timing): per kernel slot a ring of
   // KT_RING (start, stop) event pairs, [slot][set][start|stop]; sets in use
@@ -189,6 +199,7 @@ struct RecallArgs {
   const int32_t* pool_slot;
   int64_t pool_stride;
   uint8_t* pool;
+  int64_t n_slots;
   int64_t recall_base_slot;
   int32_t* table;
 };
@@ -197,7 +208,9 @@ int launch_gather(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, 
                   hipStream_t stream);
 int launch_table(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a,
                  hipStream_t stream);
-int launch_zero_counters(const kvoff_ctx* ctx, hipStream_t stream);
+// sticky = false: clear the per-call statistics; true: clear the
+// out-of-range slot count
+int launch_zero_counters(const kvoff_ctx* ctx, bool sticky, hipStream_t stream);
 
 int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& a, kvoff_stats* stats,
                hipStream_t stream);
@@ -214,7 +227,7 @@ int attend_splits(int32_t k_stride, int G);
 size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride);
 
 int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,
-                  const void* pool, const int32_t* table, const int32_t* sel_idx,
+                  const void* pool, int64_t n_slots, const int32_t* table, const int32_t* sel_idx,
                   const int32_t* sel_cnt, int32_t k_stride, float scale, float* out,
                   void* ws, hipStream_t stream);
 

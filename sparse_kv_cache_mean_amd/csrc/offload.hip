@@ -3,18 +3,21 @@
 // PulseInfer's abstract keeps most historical KV blocks in CPU DRAM; this
 // kernel produces both halves of that state for one (layer, request):
 //   - the per-block key digest in HBM: D[b][g][j] = fp32 rounding of the
-//     mean of K[t][g][j] over the block's valid tokens (fp64 sum, one fp64
-//     division by the valid-token count);
+//     mean of K[t][g][j] over the block's valid tokens (fp64 sum in token
+//     order, one fp64 division by the valid-token count);
 //   - the block record in the pinned host store, written through its mapped
 //     address: [Hkv][K,V][bs][d] elements, rows past the context end zero.
 //
-// Exactness: a block holds at most 32 fp16/bf16 values per (g, j).  Their
-// fp64 sum is exact whenever the values' binary exponents span fewer than
-// 40 binades (always for fp16), so the partial-sum order used here gives the
-// same bits as a sequential sum.
+// Summation order: each (KV head, dim) is summed in fp64 over the block's
+// valid tokens one after another in token order, the order of the plain
+// definition, so the digest bits equal a sequential sum for every finite
+// input (no reassociation: bf16 values 40 or more binades apart would round
+// differently in another order).
 //
 // One workgroup per (block, KV head); 256 threads = 16 row groups x 16 lanes
-// of 16 bytes (8 elements) across the 256-byte row.
+// of 16 bytes (8 elements) across the 256-byte row move the K and V rows to
+// the record and the key rows to LDS; then one thread per dim sums its
+// column.
 #include "kvoff_internal.h"
 
 namespace kvoff {
@@ -40,7 +43,7 @@ template <int BS>
 __global__ __launch_bounds__(256) void offload_kernel(OffloadArgs a) {
   constexpr int D = kHeadDim;
   constexpr int ROWS_PER_THREAD = BS / 16;
-  __shared__ double part[16][D];
+  __shared__ __align__(16) uint16_t k_s[BS][D];  // key rows of this (block, KV head)
 
   const int64_t b = blockIdx.x / a.Hkv;
   const int g = blockIdx.x % a.Hkv;
@@ -49,10 +52,6 @@ __global__ __launch_bounds__(256) void offload_kernel(OffloadArgs a) {
   const int rg = t >> 4;       // row group
   const int64_t tok0 = b * BS;
   const int n_valid = (int)min<int64_t>(BS, a.n_tok - tok0);
-
-  double acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
 
   uint8_t* rec = a.rec0 + b * a.rec_bytes + (int64_t)g * (2 * BS * D * 2);
 #pragma unroll
@@ -64,23 +63,15 @@ __global__ __launch_bounds__(256) void offload_kernel(OffloadArgs a) {
       const int64_t off = (tok * a.Hkv + g) * D + dg * 8;
       kx = *reinterpret_cast<const uint4*>(a.K + off);
       vx = *reinterpret_cast<const uint4*>(a.V + off);
-      const uint32_t w[4] = {kx.x, kx.y, kx.z, kx.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += widen((uint16_t)(w[e] & 0xffffu), a.bf16);
-        acc[2 * e + 1] += widen((uint16_t)(w[e] >> 16), a.bf16);
-      }
     }
+    *reinterpret_cast<uint4*>(&k_s[row][dg * 8]) = kx;
     *reinterpret_cast<uint4*>(rec + (int64_t)row * D * 2 + dg * 16) = kx;
     *reinterpret_cast<uint4*>(rec + (int64_t)(BS + row) * D * 2 + dg * 16) = vx;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][dg * 8 + e] = acc[e];
   __syncthreads();
   if (t < D) {
     double s = 0.0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += part[r][t];
+    for (int row = 0; row < n_valid; ++row) s += widen(k_s[row][t], a.bf16);
     a.digest[(b * a.Hkv + g) * D + t] = (float)(s / (double)n_valid);
   }
 }

@@ -9,13 +9,17 @@
 //  ZEROCOPY  One kernel.  Every (request, rank) item of the selection is a
 //            record (headwise: a (block, KV head) slice) copied from the
 //            mapped pinned store straight into its HBM slot with 16-byte
-//            lane loads; each workgroup moves 16 KiB pieces so tens of MB
-//            of reads are in flight over the link.  The block table is
+//            lane loads; each workgroup moves pieces of up to 16 KiB so tens
+//            of MB of reads are in flight over the link.  The block table is
 //            written by the same kernel; the plan never leaves the GPU.
+//            A pool hit whose slot lies outside [0, n_slots) gets the table
+//            entry -1 (attention skips it) and is counted in a sticky
+//            counter that the next call filling stats reports.
 //  DMA       The host reads the selection back, finds the maximal runs of
 //            consecutive missing blocks and issues one hipMemcpyAsync per
-//            run (per slice when headwise) on the stream, which the copy
-//            engines execute.
+//            run (per slice when headwise), round robin over the caller's
+//            stream and up to three copy streams of the context, which the
+//            copy engines execute; the caller's stream then waits for all.
 // A third engine, STAGED (the guide's CPU gather into pinned staging plus
 // bulk copies), is in staged.cpp.  Every engine ignores a selected block id
 // outside its request, as if the entry were unused.
@@ -47,12 +51,14 @@ struct GatherArgs {
   unsigned long long* counters;
   int64_t rec_bytes;
   int64_t item_bytes;   // rec_bytes, or slice bytes when headwise
-  int64_t piece_bytes;  // min(item_bytes, GATHER_PIECE)
+  int64_t piece_bytes;  // the largest power of two <= GATHER_PIECE dividing item_bytes
   int64_t pool_stride;
   int64_t base_slot;
+  int64_t n_slots;
   int64_t n_pieces;
   int32_t pieces_per_item;
   int32_t layer, Hkv, k_stride, hw, count;
+  int32_t flag_bad;  // count out-of-range hit slots in counters[kBadSlots]
 };
 
 struct Item {
@@ -85,6 +91,11 @@ __device__ __forceinline__ void write_table_and_count(const GatherArgs& a, int64
   int64_t entry;
   if (it.hit) {
     const int64_t ps = a.pool_slot[(int64_t)it.r * a.pool_stride + it.b];
+    if (ps < 0 || ps >= a.n_slots) {  // a resident copy outside the pool: never read
+      a.table[item] = -1;
+      if (a.flag_bad) atomicAdd(&a.counters[kBadSlots], 1ull);
+      return;
+    }
     entry = a.hw ? ps * a.Hkv + it.g : ps;
   } else {
     entry = a.hw ? it.slot * a.Hkv + it.g : it.slot;
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_kernel(GatherArgs a) {
                    (int64_t)piece * a.piece_bytes;
     const u32x4_t* s4 = reinterpret_cast<const u32x4_t*>(src);
     u32x4_t* d4 = reinterpret_cast<u32x4_t*>(dst);
-    const int n16 = (int)(a.piece_bytes / 16);  // 1024 or 512 (multiple of 256)
+    const int n16 = (int)(a.piece_bytes / 16);  // 1024, 512 or 256 (a multiple of 256)
     if (n16 == 1024) {
       const u32x4_t x0 = ld16<NTL>(s4 + tid), x1 = ld16<NTL>(s4 + tid + 256),
                     x2 = ld16<NTL>(s4 + tid + 512), x3 = ld16<NTL>(s4 + tid + 768);
@@ -163,8 +174,14 @@ __global__ void table_kernel(GatherArgs a, int64_t n_items) {
   write_table_and_count(b, item, decode_item(a, item));
 }
 
-__global__ void zero_counters_kernel(unsigned long long* c) {
-  if (threadIdx.x < 8) c[threadIdx.x] = 0ull;
+// clears the per-call statistics (counters 0..3), or with `sticky` the
+// out-of-range slot count once it has been reported
+__global__ void zero_counters_kernel(unsigned long long* c, int sticky) {
+  if (sticky) {
+    if (threadIdx.x == 0) c[kBadSlots] = 0ull;
+  } else if (threadIdx.x < 4) {
+    c[threadIdx.x] = 0ull;
+  }
 }
 
 __global__ __launch_bounds__(256) void probe_kernel(const uint4* src, int64_t n16, uint32_t* sink) {
@@ -221,10 +238,17 @@ GatherArgs make_args(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& 
   a.rec_bytes = ctx->rec_bytes;
   a.hw = r.mode == KVOFF_HEADWISE;
   a.item_bytes = a.hw ? ctx->slice_bytes : ctx->rec_bytes;
-  a.piece_bytes = a.item_bytes < GATHER_PIECE ? a.item_bytes : GATHER_PIECE;
+  // Pieces tile the item exactly.  A record is Hkv slices of 2*bs*d*es
+  // bytes (8 KiB at 16-token blocks, 16 KiB at 32), so a record of an odd
+  // number of 8 KiB slices (Hkv = 3 at 16-token blocks: 24 KiB) is moved in
+  // 8 KiB pieces, not in one 16 KiB piece that would leave its tail behind.
+  a.piece_bytes = GATHER_PIECE;
+  while (a.piece_bytes > GATHER_THREADS * 16 && a.item_bytes % a.piece_bytes != 0) a.piece_bytes /= 2;
   a.pieces_per_item = (int32_t)(a.item_bytes / a.piece_bytes);
   a.pool_stride = r.pool_stride;
   a.base_slot = r.recall_base_slot;
+  a.n_slots = r.n_slots;
+  a.flag_bad = 1;
   a.layer = r.layer;
   a.Hkv = ctx->cfg.num_kv_heads;
   a.k_stride = r.k_stride;
@@ -236,8 +260,9 @@ GatherArgs make_args(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& 
 
 }  // namespace
 
-int launch_zero_counters(const kvoff_ctx* ctx, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, ctx->d_counters);
+int launch_zero_counters(const kvoff_ctx* ctx, bool sticky, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, ctx->d_counters,
+                     sticky ? 1 : 0);
   KVOFF_HIP(hipGetLastError());
   return KVOFF_OK;
 }
@@ -246,6 +271,9 @@ int launch_gather(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, 
                   hipStream_t stream) {
   GatherArgs a = make_args(ctx, b, r);
   a.count = count ? 1 : 0;
+  if (a.item_bytes % a.piece_bytes != 0 || a.piece_bytes % (GATHER_THREADS * 16) != 0)
+    return fail(KVOFF_ESTATE, "gather: %lld-byte items do not split into whole pieces",
+                (long long)a.item_bytes);
   if (a.n_pieces == 0) return KVOFF_OK;
   const int64_t cap = gather_grid_cap();
   const unsigned grid = (unsigned)(a.n_pieces < cap ? a.n_pieces : cap);
@@ -273,6 +301,7 @@ int launch_gather(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, 
 int launch_table(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r,
                  hipStream_t stream) {
   GatherArgs a = make_args(ctx, b, r);
+  a.flag_bad = 0;  // the host engines check the hit slots themselves
   const int64_t n_items = a.n_pieces / a.pieces_per_item;
   if (n_items == 0) return KVOFF_OK;
   hipLaunchKernelGGL(table_kernel, dim3((unsigned)((n_items + 255) / 256)), dim3(256), 0, stream,
@@ -281,13 +310,26 @@ int launch_table(const kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r,
   return KVOFF_OK;
 }
 
+// Copy streams of the DMA engine: the caller's stream plus up to three the
+// context owns (non-blocking, default priority), which the box's four
+// hardware queues per process can all serve.  KVOFF_DMA_STREAMS (1..4)
+// overrides the count for measurements.
+int dma_streams() {
+  static const int n = [] {
+    const char* e = std::getenv("KVOFF_DMA_STREAMS");
+    const int v = e ? std::atoi(e) : 0;
+    return v >= 1 && v <= 1 + kDmaSideStreams ? v : 1 + kDmaSideStreams;
+  }();
+  return n;
+}
+
 int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_stats* stats,
                hipStream_t stream) {
   const bool hw = r.mode == KVOFF_HEADWISE;
   const int Hkv = ctx->cfg.num_kv_heads;
   const int sets = hw ? Hkv : 1;
   const size_t n_sel = (size_t)b.n * sets * r.k_stride;
-  std::vector<int32_t> cnt(b.n), sel(n_sel);
+  std::vector<int32_t> cnt(b.n), sel(n_sel), pslot;
   std::vector<uint8_t> hit;
   // the selection must be complete before the host can plan the copies
   // (read back on the same stream, so no other stream is waited for)
@@ -297,13 +339,26 @@ int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_sta
                            stream));
   if (r.pool_hit) {
     hit.resize((size_t)b.n * r.pool_stride);
+    pslot.resize(hit.size());
     KVOFF_HIP(hipMemcpyAsync(hit.data(), r.pool_hit, hit.size(), hipMemcpyDeviceToHost, stream));
+    KVOFF_HIP(hipMemcpyAsync(pslot.data(), r.pool_slot, pslot.size() * sizeof(int32_t),
+                             hipMemcpyDeviceToHost, stream));
   }
   KVOFF_HIP(hipStreamSynchronize(stream));
+  // every earlier command of `stream` has completed, so the side streams may
+  // start at once; `stream` waits for their last copies below
+  const int n_streams = dma_streams();
+  for (int k = 0; k + 1 < n_streams; ++k) {
+    if (!ctx->dma_stream[k]) {
+      KVOFF_HIP(hipStreamCreateWithFlags(&ctx->dma_stream[k], hipStreamNonBlocking));
+      KVOFF_HIP(hipEventCreateWithFlags(&ctx->dma_done[k], hipEventDisableTiming));
+    }
+  }
   int st = launch_table(ctx, b, r, stream);
   if (st) return st;
   const int64_t item = hw ? ctx->slice_bytes : ctx->rec_bytes;
-  int64_t n_selected = 0, n_hits = 0, n_items = 0, n_transfers = 0;
+  int64_t n_selected = 0, n_hits = 0, n_items = 0, n_transfers = 0, n_bad = 0;
+  bool used[1 + kDmaSideStreams] = {};
   for (int ri = 0; ri < b.n; ++ri) {
     const ReqHost& rq = ctx->reqs[b.id[ri]];
     const uint8_t* rec_l = ctx->store + (size_t)(rq.rec_base + (int64_t)r.layer * rq.nb) * ctx->rec_bytes;
@@ -318,26 +373,39 @@ int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_sta
           ++i;
           continue;
         }
-        ++n_selected;
         if (is_hit(s[i])) {
-          ++n_hits;
+          const int64_t ps = pslot[(size_t)ri * r.pool_stride + s[i]];
+          if (ps < 0 || ps >= r.n_slots) {
+            ++n_bad;  // table entry -1 (table_kernel): neither read nor moved
+          } else {
+            ++n_selected;
+            ++n_hits;
+          }
           ++i;
           continue;
         }
         int j = i + 1;
         if (!hw)
           while (j < K && valid(s[j]) && s[j] == s[j - 1] + 1 && !is_hit(s[j])) ++j;
-        n_selected += j - i - 1;
+        n_selected += j - i;
         const int64_t slot = r.recall_base_slot + (int64_t)ri * r.k_stride + i;
         const uint8_t* src = rec_l + (size_t)s[i] * ctx->rec_bytes + (hw ? (size_t)g * item : 0);
         uint8_t* dst = r.pool + (hw ? (slot * Hkv + g) * item : slot * ctx->rec_bytes);
         const size_t bytes = (size_t)(j - i) * item;
-        KVOFF_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, stream));
+        const int k = (int)(n_transfers % n_streams);  // round robin over the copy streams
+        used[k] = true;
+        KVOFF_HIP(hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice,
+                                 k == 0 ? stream : ctx->dma_stream[k - 1]));
         n_items += j - i;
         ++n_transfers;
         i = j;
       }
     }
+  }
+  for (int k = 1; k < n_streams; ++k) {
+    if (!used[k]) continue;
+    KVOFF_HIP(hipEventRecord(ctx->dma_done[k - 1], ctx->dma_stream[k - 1]));
+    KVOFF_HIP(hipStreamWaitEvent(stream, ctx->dma_done[k - 1], 0));
   }
   if (stats) {
     KVOFF_HIP(hipStreamSynchronize(stream));
@@ -347,6 +415,9 @@ int recall_dma(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_sta
     stats->transfers = n_transfers;
     stats->bytes = n_items * item;
   }
+  if (n_bad)
+    return fail(KVOFF_ESTATE, "%lld pool hits name a slot outside [0, %lld): table entries -1",
+                (long long)n_bad, (long long)r.n_slots);
   return KVOFF_OK;
 }
 

@@ -176,6 +176,14 @@ struct Piece {  // one contiguous source range of the store
   size_t bytes;
 };
 
+// the call's status once its work is enqueued: ESTATE when pool hits named
+// slots outside the pool (their table entries are -1)
+int bad_slots(int64_t n_bad, int64_t n_slots) {
+  if (!n_bad) return KVOFF_OK;
+  return fail(KVOFF_ESTATE, "%lld pool hits name a slot outside [0, %lld): table entries -1",
+              (long long)n_bad, (long long)n_slots);
+}
+
 int ensure_host(void** buf, size_t* cap, size_t need) {
   if (*cap >= need) return KVOFF_OK;
   if (*buf) KVOFF_HIP(hipHostFree(*buf));
@@ -231,7 +239,7 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   if (st) return st;
   int32_t* table = (int32_t*)ctx->table_host;
   std::vector<Piece> pieces;
-  int64_t n_items = 0, n_hits = 0, n_selected = 0;
+  int64_t n_items = 0, n_hits = 0, n_selected = 0, n_bad = 0;
   for (int ri = 0; ri < b.n; ++ri) {
     const ReqHost& rq = ctx->reqs[b.id[ri]];
     const uint8_t* rec_l = ctx->store + (size_t)(rq.rec_base + (int64_t)r.layer * rq.nb) * ctx->rec_bytes;
@@ -244,13 +252,19 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
           table[row + i] = -1;
           continue;
         }
-        ++n_selected;
         if (r.pool_hit && hit[(size_t)ri * r.pool_stride + blk]) {
           const int64_t ps = pslot[(size_t)ri * r.pool_stride + blk];
+          if (ps < 0 || ps >= r.n_slots) {  // a resident copy outside the pool: never read
+            table[row + i] = -1;
+            ++n_bad;
+            continue;
+          }
           table[row + i] = (int32_t)(hw ? ps * Hkv + g : ps);
+          ++n_selected;
           ++n_hits;
           continue;
         }
+        ++n_selected;
         table[row + i] = (int32_t)(hw ? r.recall_base_slot * Hkv + n_items : r.recall_base_slot + n_items);
         const uint8_t* src = rec_l + (size_t)blk * ctx->rec_bytes + (hw ? (size_t)g * item : 0);
         if (!pieces.empty() && pieces.back().src + pieces.back().bytes == src)
@@ -272,7 +286,7 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
       KVOFF_HIP(hipStreamSynchronize(stream));
       *stats = kvoff_stats{n_selected, n_hits, 0, 0, 0};
     }
-    return KVOFF_OK;
+    return bad_slots(n_bad, r.n_slots);
   }
 
   // Chunks of the staging buffer, each one bulk copy: 1 MiB, then 3 MiB,
@@ -358,7 +372,7 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
     KVOFF_HIP(hipStreamSynchronize(stream));
     *stats = kvoff_stats{n_selected, n_hits, n_items, n_transfers, n_items * item};
   }
-  return KVOFF_OK;
+  return bad_slots(n_bad, r.n_slots);
 }
 
 }  // namespace kvoff

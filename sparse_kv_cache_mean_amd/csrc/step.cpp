@@ -29,6 +29,7 @@
 // the others are still crossing the link.
 #include <algorithm>
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "kvoff_internal.h"
@@ -60,8 +61,19 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     }
     if (!A->pool_hit_dev != !A->pool_slot_dev)
       return fail(KVOFF_EINVAL, "pool_hit_dev and pool_slot_dev must both be given or both NULL");
-    if (L > 1 && A->recall_base_slot[0] == A->recall_base_slot[1] && A->copy_stream != A->compute_stream)
-      return fail(KVOFF_EINVAL, "overlapped layers need two distinct recall regions");
+    // overlapped layers write one buffer set's recall region while attention
+    // reads the other's: the two regions of n_req * k_stride slots must not
+    // share a slot
+    const int64_t region = (int64_t)A->n_req * A->k_stride;
+    const int64_t gap = A->recall_base_slot[0] > A->recall_base_slot[1]
+                            ? A->recall_base_slot[0] - A->recall_base_slot[1]
+                            : A->recall_base_slot[1] - A->recall_base_slot[0];
+    if (L > 1 && A->copy_stream != A->compute_stream && gap < region)
+      return fail(KVOFF_EINVAL,
+                  "overlapped layers need disjoint recall regions: bases %lld and %lld are %lld "
+                  "slots apart, a region is %lld",
+                  (long long)A->recall_base_slot[0], (long long)A->recall_base_slot[1],
+                  (long long)gap, (long long)region);
 
     hipStream_t cs = (hipStream_t)A->compute_stream;
     hipStream_t xs0 = (hipStream_t)A->copy_stream;
@@ -101,6 +113,13 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
         if (A->req_ids[r] < 0 || A->req_ids[r] >= (int)ctx->reqs.size())
           return fail(KVOFF_ESTATE, "request id %d is not registered", A->req_ids[r]);
     }
+    // every (layer, request) offloaded, so that the only ESTATE a recall
+    // below can return is the pool-slot report, after enqueuing its work
+    for (int li = 0; li < L; ++li)
+      for (int r = 0; r < A->n_req; ++r)
+        if (!ctx->offloaded[(size_t)A->req_ids[r] * ctx->cfg.num_layers + A->layer_begin + li])
+          return fail(KVOFF_ESTATE, "layer %d of request %d was not offloaded", A->layer_begin + li,
+                      A->req_ids[r]);
     // issue order of the groups for layer li: fewest blocks to transfer first
     // (stable, so equal groups keep batch order)
     auto order_for = [&](int li) {
@@ -138,6 +157,11 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
     const int sets = layout_of(A->mode) == KVOFF_HEADWISE ? ctx->cfg.num_kv_heads : 1;
     const int64_t q_row = (int64_t)ctx->cfg.num_q_heads * ctx->cfg.head_dim;  // elements per request
 
+    // a recall that reports pool hits outside the pool (ESTATE, only known
+    // when stats are filled) has still enqueued its work: the step goes on
+    // and returns that status at the end
+    int deferred = KVOFF_OK;
+    std::string deferred_msg;
     auto recall_l = [&](int li) -> int {
       const int buf = li & 1;
       // this layer's pool maps (a layer may have none)
@@ -158,6 +182,11 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
             A->pool_stride, A->slot_pool_dev, A->n_slots,
             A->recall_base_slot[buf] + (int64_t)g.r0 * A->k_stride, A->block_table_dev[buf] + sel_off,
             A->engine, A->stats ? &st_l : nullptr, xs);
+        if (st == KVOFF_ESTATE && deferred == KVOFF_OK) {
+          deferred = st;
+          deferred_msg = kvoff_last_error();
+          st = KVOFF_OK;
+        }
         if (st) return st;
         if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 4), xs));
         if (A->stats) {
@@ -181,7 +210,7 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
         if (A->timing) KVOFF_HIP(hipEventRecord(tev(li, gi, 1), cs));
         int st = kvoff_sparse_decode(
             ctx, g.n, A->req_ids + g.r0, A->mode,
-            (const uint8_t*)A->q_dev[li] + g.r0 * q_row * 2, A->slot_pool_dev,
+            (const uint8_t*)A->q_dev[li] + g.r0 * q_row * 2, A->slot_pool_dev, A->n_slots,
             A->block_table_dev[buf] + sel_off, A->sel_idx_dev[buf] + sel_off,
             A->sel_cnt_dev[buf] + g.r0, A->k_stride, A->scale, A->out_dev[li] + g.r0 * q_row,
             A->ws_dev, A->ws_bytes, cs);
@@ -218,6 +247,7 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
       }
       T.step_ms = T.max_request_done_ms;
     }
+    if (deferred) return fail(deferred, "%s", deferred_msg.c_str());
     return KVOFF_OK;
   });
 }

@@ -137,7 +137,7 @@ static void run(int dtype) {
   KVOK(kvoff_select(ctx, 0, 1, ids, dq, dD, NB, topk, KVOFF_SOLOHEAD, dS, dsel, dcnt, TOPK, NULL));
   KVOK(kvoff_recall(ctx, 0, 1, ids, KVOFF_SOLOHEAD, dsel, dcnt, TOPK, NULL, NULL, 0, pool, n_slots,
                     0, dtab, KVOFF_ENGINE_ZEROCOPY, &st, NULL));
-  KVOK(kvoff_sparse_decode(ctx, 1, ids, KVOFF_SOLOHEAD, dq, pool, dtab, dsel, dcnt, TOPK,
+  KVOK(kvoff_sparse_decode(ctx, 1, ids, KVOFF_SOLOHEAD, dq, pool, n_slots, dtab, dsel, dcnt, TOPK,
                            (float)(1.0 / sqrt((double)D)), dout, ws, ws_bytes, NULL));
   HIPOK(hipDeviceSynchronize());
 
@@ -255,7 +255,7 @@ static void run_step(int dtype) {
                       TOPK, NULL));
     KVOK(kvoff_recall(ctx, l, 1, ids, KVOFF_SOLOHEAD, dsel[0], dcnt[0], TOPK, NULL, NULL, 0, pool,
                       n_slots, 0, dtab[0], KVOFF_ENGINE_ZEROCOPY, NULL, NULL));
-    KVOK(kvoff_sparse_decode(ctx, 1, ids, KVOFF_SOLOHEAD, dq[l], pool, dtab[0], dsel[0], dcnt[0], TOPK,
+    KVOK(kvoff_sparse_decode(ctx, 1, ids, KVOFF_SOLOHEAD, dq[l], pool, n_slots, dtab[0], dsel[0], dcnt[0], TOPK,
                              scale, dref[l], ws, ws_bytes, NULL));
   }
   HIPOK(hipDeviceSynchronize());

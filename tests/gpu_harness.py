@@ -170,7 +170,7 @@ def run_layer(c: Case, l: int, mode: int, bufs: Buffers, engine: int = kv.KVOFF_
                             c.pool_slot.get(l) if with_pool_hits else None, c.nb_max,
                             c.pool, c.n_slots, c.recall_base[region], bufs.table, engine,
                             want_stats=want_stats, stream=stream)
-    kv.kvoff_sparse_decode(c.ctx, c.rids, mode, c.q[l], c.pool, bufs.table, bufs.sel_idx,
+    kv.kvoff_sparse_decode(c.ctx, c.rids, mode, c.q[l], c.pool, c.n_slots, bufs.table, bufs.sel_idx,
                            bufs.sel_cnt, c.k_stride, 1.0 / math.sqrt(c.s.d), bufs.out, bufs.ws,
                            stream=stream)
     return stats

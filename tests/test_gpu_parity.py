@@ -595,7 +595,7 @@ def test_error_paths_on_device():
                             bufs.table)
         assert e.value.status == kv.KVOFF_ERANGE
         with pytest.raises(kv.KvoffError) as e:  # workspace too small
-            kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, bufs.table,
+            kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, c.n_slots, bufs.table,
                                    bufs.sel_idx, bufs.sel_cnt, c.k_stride, 0.1, bufs.out,
                                    bufs.ws[:4])
         assert e.value.status == kv.KVOFF_ERANGE
@@ -653,7 +653,7 @@ def test_out_of_range_block_ids_are_unused_entries(engine):
         st = kv.kvoff_recall(c.ctx, 0, c.rids, kv.KVOFF_SOLOHEAD, bufs.sel_idx, bufs.sel_cnt,
                              c.k_stride, None, None, 0, c.pool, c.n_slots, c.recall_base[0],
                              bufs.table, engine, want_stats=True)
-        kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, bufs.table,
+        kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, c.n_slots, bufs.table,
                                bufs.sel_idx, bufs.sel_cnt, c.k_stride, 1.0 / math.sqrt(s.d),
                                bufs.out, bufs.ws)
         torch.cuda.synchronize()
@@ -701,6 +701,9 @@ def test_step_error_paths():
         for kw, status in ((dict(layer_end=len(layers) + 1), kv.KVOFF_ERANGE),
                            (dict(layer_begin=-1), kv.KVOFF_ERANGE),
                            (dict(recall_base_slot=(0, 0)), kv.KVOFF_EINVAL),
+                           # regions of B * k_stride slots that overlap by one slot
+                           (dict(recall_base_slot=(0, c.B * c.k_stride - 1)), kv.KVOFF_EINVAL),
+                           (dict(recall_base_slot=(c.B * c.k_stride - 1, 0)), kv.KVOFF_EINVAL),
                            (dict(req_ids=[c.rids[0], 99]), kv.KVOFF_ESTATE),
                            (dict(q=[c.q[l] for l in layers[:-1]] + [None]), kv.KVOFF_EINVAL)):
             with pytest.raises(kv.KvoffError) as e:
