@@ -287,6 +287,27 @@ int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, i
                         const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
                         float* out_dev, void* ws_dev, size_t ws_bytes, void* stream);
 
+/* kvoff_sparse_decode without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  The split partials go to a scratch
+ * array of KVOFF_NOALLOC_SCRATCH_BYTES that the library holds in device
+ * memory, one per GPU for the life of the process (its address is looked up
+ * by kvoff_create); the call allocates nothing.  Arguments and results as
+ * kvoff_sparse_decode.  Every call on one GPU uses that GPU's one array:
+ * calls that overlap in time on the same GPU (two streams, or two host
+ * threads, whatever the context) race and give wrong results; calls ordered
+ * on one stream do not.  Nothing in the array needs to start at zero, and
+ * it keeps the last call's partials.  Errors: as kvoff_sparse_decode, and
+ * ERANGE when kvoff_workspace_size(ctx, KVOFF_CALL_SPARSE_DECODE, n_req,
+ * k_stride, mode) exceeds KVOFF_NOALLOC_SCRATCH_BYTES (16 MiB: n_req * Hq *
+ * splits <= 32,263 partial rows of 520 bytes). */
+#define KVOFF_NOALLOC_SCRATCH_BYTES (16u << 20)
+int kvoff_sparse_decode_noalloc(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids,
+                                int32_t mode, const void* q_dev, const void* slot_pool_dev,
+                                int64_t n_slots, const int32_t* block_table_dev,
+                                const int32_t* sel_idx_dev, const int32_t* sel_cnt_dev,
+                                int32_t k_stride, float scale, float* out_dev, void* stream);
+
 enum { KVOFF_CALL_SPARSE_DECODE = 1, KVOFF_CALL_STEP = 2 };
 
 /* Scratch bytes a call needs for the given batch (0 if none). */

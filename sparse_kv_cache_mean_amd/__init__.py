@@ -29,6 +29,7 @@ KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA, KVOFF_ENGINE_STAGED = 0, 1, 2
 KVOFF_HOST_COHERENT, KVOFF_HOST_NONCOHERENT = 0, 1
 KVOFF_CALL_SPARSE_DECODE, KVOFF_CALL_STEP = 1, 2
 KVOFF_MAX_BATCH = 128
+KVOFF_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "kvoff_create", "kvoff_destroy", "kvoff_record_bytes", "kvoff_set_consensus_lambda",
@@ -38,7 +39,7 @@ EXPORTS = (
     "kvoff_sparse_decode", "kvoff_workspace_size", "kvoff_step", "kvoff_probe_read",
     "kvoff_strerror", "kvoff_last_error", "kvoff_admission_defaults", "kvoff_admission_plan",
     "kvoff_make_resident", "kvoff_release_resident", "kvoff_set_kernel_timing",
-    "kvoff_get_kernel_times",
+    "kvoff_get_kernel_times", "kvoff_sparse_decode_noalloc",
 )
 
 
@@ -140,6 +141,8 @@ def lib() -> ctypes.CDLL:
                                i64, _vp, i32, _vp, _vp]
     L.kvoff_sparse_decode.argtypes = [_vp, i32, _vp, i32, _vp, _vp, i64, _vp, _vp, _vp, i32, f32,
                                       _vp, _vp, sz, _vp]
+    L.kvoff_sparse_decode_noalloc.argtypes = [_vp, i32, _vp, i32, _vp, _vp, i64, _vp, _vp, _vp,
+                                              i32, f32, _vp, _vp]
     L.kvoff_workspace_size.argtypes = [_vp, i32, i32, i32, i32]
     L.kvoff_workspace_size.restype = sz
     L.kvoff_step.argtypes = [_vp, P(kvoff_step_args)]
@@ -159,6 +162,7 @@ def lib() -> ctypes.CDLL:
     for name in ("kvoff_create", "kvoff_destroy", "kvoff_register_request", "kvoff_host_record",
                  "kvoff_set_consensus_lambda", "kvoff_set_attention_qk",
                  "kvoff_offload_blocks", "kvoff_select", "kvoff_recall", "kvoff_sparse_decode",
+                 "kvoff_sparse_decode_noalloc",
                  "kvoff_step", "kvoff_probe_read", "kvoff_attention_mass", "kvoff_admission_plan", "kvoff_make_resident",
                  "kvoff_release_resident", "kvoff_set_kernel_timing", "kvoff_get_kernel_times"):
         getattr(L, name).restype = ctypes.c_int
@@ -288,6 +292,16 @@ def kvoff_sparse_decode(ctx: int, req_ids: Sequence[int], mode: int, q, slot_poo
     _check(lib().kvoff_sparse_decode(ctx, len(req_ids), ids, mode, _ptr(q), _ptr(slot_pool),
                                      n_slots, _ptr(block_table), _ptr(sel_idx), _ptr(sel_cnt), k_stride,
                                      scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def kvoff_sparse_decode_noalloc(ctx: int, req_ids: Sequence[int], mode: int, q, slot_pool,
+                                n_slots: int, block_table, sel_idx, sel_cnt, k_stride: int,
+                                scale: float, out, stream=None) -> None:
+    ids = _i32_array(req_ids)
+    _check(lib().kvoff_sparse_decode_noalloc(ctx, len(req_ids), ids, mode, _ptr(q),
+                                             _ptr(slot_pool), n_slots, _ptr(block_table),
+                                             _ptr(sel_idx), _ptr(sel_cnt), k_stride, scale,
+                                             _ptr(out), _stream(stream)))
 
 
 def kvoff_step(ctx: int, *, layer_begin: int, layer_end: int, req_ids: Sequence[int],

@@ -129,6 +129,8 @@ int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
         status = fail(KVOFF_EHIP, "hipGetDevice failed");
         break;
       }
+      // kvoff_sparse_decode_noalloc's scratch: its address on this device
+      if ((status = attend_scratch_address(ctx->device, &ctx->noalloc_scratch)) != KVOFF_OK) break;
       size_t bytes = (size_t)c.host_capacity_blocks * (size_t)ctx->rec_bytes;
       unsigned flags = hipHostMallocMapped | hipHostMallocPortable |
                        (c.host_mem_kind == KVOFF_HOST_COHERENT ? hipHostMallocCoherent
@@ -414,35 +416,69 @@ size_t kvoff_workspace_size(const kvoff_ctx* ctx, int32_t call, int32_t n_req, i
   return 0;
 }
 
+}  // extern "C"
+
+// kvoff_sparse_decode and its no-alloc form: ws_dev is the caller's
+// workspace or the library's scratch array (noalloc), ws_bytes its size
+static int sparse_decode_impl(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, int32_t mode,
+                              const void* q_dev, const void* slot_pool_dev, int64_t n_slots,
+                              const int32_t* block_table_dev, const int32_t* sel_idx_dev,
+                              const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
+                              float* out_dev, void* ws_dev, size_t ws_bytes, bool noalloc,
+                              void* stream) {
+  if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
+  BatchIds b;
+  int st = make_batch(ctx, n_req, req_ids, &b);
+  if (st) return st;
+  if (n_req == 0) return KVOFF_OK;
+  if (!q_dev || !slot_pool_dev || !block_table_dev || !sel_idx_dev || !sel_cnt_dev || !out_dev)
+    return fail(KVOFF_EINVAL, "NULL buffer argument");
+  mode = layout_of(mode);  // consensus modes use the layout of their scope
+  if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
+  if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
+  if (n_slots < 1 || n_slots > INT32_MAX / ctx->cfg.num_kv_heads)
+    return fail(KVOFF_EINVAL, "n_slots %lld outside [1, %d]", (long long)n_slots,
+                INT32_MAX / ctx->cfg.num_kv_heads);
+  size_t need = attend_ws_bytes(ctx, n_req, k_stride);
+  if (noalloc && need > ws_bytes)
+    return fail(KVOFF_ERANGE, "split partials of %zu bytes exceed the %zu-byte scratch array",
+                need, ws_bytes);
+  if (need > 0 && (!ws_dev || ws_bytes < need))
+    return fail(KVOFF_ERANGE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  KVOFF_HIP(hipSetDevice(ctx->device));
+  st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, n_slots, block_table_dev, sel_idx_dev,
+                     sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
+  if (st) return st;
+  if ((st = kernel_timing_advance(ctx, KT_ATTEND))) return st;
+  if ((st = kernel_timing_advance(ctx, KT_COMBINE))) return st;
+  return KVOFF_OK;
+}
+
+extern "C" {
+
 int kvoff_sparse_decode(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, int32_t mode,
                         const void* q_dev, const void* slot_pool_dev, int64_t n_slots,
                         const int32_t* block_table_dev, const int32_t* sel_idx_dev,
                         const int32_t* sel_cnt_dev, int32_t k_stride, float scale,
                         float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   return guarded([&]() -> int {
+    return sparse_decode_impl(ctx, n_req, req_ids, mode, q_dev, slot_pool_dev, n_slots,
+                              block_table_dev, sel_idx_dev, sel_cnt_dev, k_stride, scale, out_dev,
+                              ws_dev, ws_bytes, false, stream);
+  });
+}
+
+int kvoff_sparse_decode_noalloc(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids,
+                                int32_t mode, const void* q_dev, const void* slot_pool_dev,
+                                int64_t n_slots, const int32_t* block_table_dev,
+                                const int32_t* sel_idx_dev, const int32_t* sel_cnt_dev,
+                                int32_t k_stride, float scale, float* out_dev, void* stream) {
+  return guarded([&]() -> int {
     if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
-    BatchIds b;
-    int st = make_batch(ctx, n_req, req_ids, &b);
-    if (st) return st;
-    if (n_req == 0) return KVOFF_OK;
-    if (!q_dev || !slot_pool_dev || !block_table_dev || !sel_idx_dev || !sel_cnt_dev || !out_dev)
-      return fail(KVOFF_EINVAL, "NULL buffer argument");
-    mode = layout_of(mode);  // consensus modes use the layout of their scope
-    if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
-    if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
-    if (n_slots < 1 || n_slots > INT32_MAX / ctx->cfg.num_kv_heads)
-      return fail(KVOFF_EINVAL, "n_slots %lld outside [1, %d]", (long long)n_slots,
-                  INT32_MAX / ctx->cfg.num_kv_heads);
-    size_t need = attend_ws_bytes(ctx, n_req, k_stride);
-    if (need > 0 && (!ws_dev || ws_bytes < need))
-      return fail(KVOFF_ERANGE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
-    KVOFF_HIP(hipSetDevice(ctx->device));
-    st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, n_slots, block_table_dev, sel_idx_dev,
-                       sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
-    if (st) return st;
-    if ((st = kernel_timing_advance(ctx, KT_ATTEND))) return st;
-    if ((st = kernel_timing_advance(ctx, KT_COMBINE))) return st;
-    return KVOFF_OK;
+    if (!ctx->noalloc_scratch) return fail(KVOFF_ESTATE, "the context has no scratch address");
+    return sparse_decode_impl(ctx, n_req, req_ids, mode, q_dev, slot_pool_dev, n_slots,
+                              block_table_dev, sel_idx_dev, sel_cnt_dev, k_stride, scale, out_dev,
+                              ctx->noalloc_scratch, KVOFF_NOALLOC_SCRATCH_BYTES, true, stream);
   });
 }
 

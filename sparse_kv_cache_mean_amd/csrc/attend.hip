@@ -44,10 +44,42 @@
 // workgroup instead needs a device-scope release per workgroup, which on this
 // part writes back the L2 that the recall just filled; measured 8x slower.)
 #include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "kvoff_internal.h"
 
+// Split partials of kvoff_sparse_decode_noalloc: a file-scope device array
+// instead of a caller workspace, one copy per GPU for the life of the
+// process.  Host code never uses the name itself (on the host it is only a
+// stand-in): its device address comes from hipGetSymbolAddress, once per
+// device (kvoff::attend_scratch_address).
+static __device__ __align__(256) unsigned char scratch[KVOFF_NOALLOC_SCRATCH_BYTES];
+
 namespace kvoff {
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_dev;  // device address of `scratch`, per device
+}  // namespace
+
+int attend_scratch_address(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0) return fail(KVOFF_EINVAL, "device %d", device);
+  if ((int)g_scratch_dev.size() <= device) g_scratch_dev.resize((size_t)device + 1, nullptr);
+  if (!g_scratch_dev[device]) {
+    int cur = -1;
+    KVOFF_HIP(hipGetDevice(&cur));
+    if (cur != device) return fail(KVOFF_ESTATE, "device %d is not current (%d is)", device, cur);
+    void* p = nullptr;
+    KVOFF_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(KVOFF_EHIP, "no device address for the attention scratch");
+    g_scratch_dev[device] = p;
+  }
+  *out = g_scratch_dev[device];
+  return KVOFF_OK;
+}
+
 namespace {
 
 constexpr int ATT_WAVES = 4;

@@ -88,6 +88,7 @@ struct kvoff_ctx {
   hipEvent_t ev_stage = nullptr;            // behind the last staged copy
   std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
+  void* noalloc_scratch = nullptr;          // device address of the attention scratch array
   hipStream_t copy2 = nullptr;              // kvoff_step's own second copy stream (lazy)
   hipStream_t dma_stream[kvoff::kDmaSideStreams] = {};  // DMA engine's copy streams (lazy)
   hipEvent_t dma_done[kvoff::kDmaSideStreams] = {};     // behind each one's last copy
@@ -221,6 +222,10 @@ void stage_pool_destroy(kvoff_ctx* ctx);
 int launch_mass(const kvoff_ctx* ctx, const BatchIds& b, int32_t layer, int32_t mode,
                 const void* q_dev, const int32_t* sel_idx, const int32_t* sel_cnt,
                 int32_t k_stride, float scale, double* mass_dev, hipStream_t stream);
+
+// device address of the attention's file-scope scratch array on `device`
+// (which must be current), looked up once per device
+int attend_scratch_address(int device, void** out);
 
 // split policy of the attention kernel: number of splits per (request, KV head)
 int attend_splits(int32_t k_stride, int G);
