@@ -40,9 +40,9 @@ METRIC = "sparse decode layer-steps/s; recall GB/s host→HBM vs link peak; HBM 
 # workload, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE; summary
 # and calibration in profiles/llama3-8b-layer_pmc_traffic.md).  Valid only for
 # the recall source it was taken with: reported as null once that changes.
-GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65604.9, "write_kib": 131076.2,
+GATHER_PMC = {"workload": ("llama3-8b-layer", 4), "fetch_kib": 65605.2, "write_kib": 131082.5,
               "fetch_scale": 1.9999, "write_scale": 1.0000,
-              "recall_src_sha256": "e4f84d2d465c8c7cb8540f214126917d14080726170791c7d2ae292955dcde73"}
+              "recall_src_sha256": "b79e692fb4abc5059c50b5a54cce73825f65cab820a3bc4647a8387842908398"}
 
 
 def gather_traffic_bytes(workload, layers):
@@ -77,7 +77,13 @@ def parse():
     p.add_argument("--attn-qk", choices=["mfma", "valu"], default="mfma",
                    help="what computes the attention's QK^T")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="oracle time on host cores for the headline workload's baseline")
+    p.add_argument("--configs", default="1,3,4,5",
+                   help="other workloads measured after the headline, by number (or 'none'); "
+                        "each adds an entry to the line's configs object")
+    p.add_argument("--config-cpu-seconds", type=float, default=6.0,
+                   help="oracle time on host cores for each other workload's baseline")
     p.add_argument("--no-overlap", action="store_true",
                    help="time the serial order on one stream as the value instead of "
                         "kvoff_step (every gather then runs alone: clean kernel traces)")
@@ -97,6 +103,15 @@ def parse():
     args = p.parse_args()
     if args.steps < 1 or args.warmup < 0:
         p.error("--steps must be at least 1 and --warmup at least 0")
+    if args.configs.strip().lower() in ("", "none"):
+        args.config_list = []
+    else:
+        try:
+            args.config_list = [int(x) for x in args.configs.split(",")]
+        except ValueError:
+            p.error("--configs takes workload numbers such as 1,3,4,5, or none")
+        if any(n not in CONFIG_LAYERS for n in args.config_list):
+            p.error(f"--configs: workloads {sorted(CONFIG_LAYERS)} (2 is the headline)")
     return args
 
 
@@ -239,23 +254,34 @@ def host_cpu():
             "numa_nodes": nodes}
 
 
-def cpu_baseline(sp, inputs, B, budget_s):
+def cpu_baseline(sp, inputs, B, budget_s, keys=None, threads=None):
     """The oracle, as it is, on host cores: one request's layer-step (score,
-    select, record gather of the selected blocks, fp32 attention) per call.
-    Timed twice for about budget_s / 2 seconds each: on one thread, then with
-    one worker thread per core running independent requests (the oracle is
-    plain C with no shared state; ctypes releases the interpreter lock while
-    it runs).  Scaled to layer-steps/s; the value is the threaded figure."""
+    select, record gather of the selected blocks, fp32 attention) per call,
+    over the (layer, request) slices `keys` of `inputs` (default: layer 0 of
+    every request), in that order.  Timed twice for about budget_s / 2
+    seconds each: on one thread, then with one worker thread per core running
+    independent requests (the oracle is plain C with no shared state; ctypes
+    releases the interpreter lock while it runs).  Each leg is scaled to
+    layer-steps/s from its mean time per request-step: a layer-step is B
+    request-steps.  When a leg ends before it has visited every slice, its
+    mean is over the slices visited, which the sample string says.  The value
+    is the threaded figure."""
     import oracle
     from concurrent.futures import ThreadPoolExecutor
+    keys = keys or [(0, r) for r in range(B)]
+    threads = threads or max(1, min(16, os.cpu_count() or 1))
     digests = {}
-    for r in range(B):
-        lr = inputs[(0, r)]
-        digests[r] = oracle.digest(lr.K, sp.dtype, sp.bs)  # setup, not timed
 
-    def request_step(r):
-        lr = inputs[(0, r)]
-        S = oracle.score(lr.q, sp.dtype, digests[r])
+    def digest(k):
+        lr = inputs[k]
+        digests[k] = oracle.digest(lr.K, sp.dtype, sp.bs)  # setup, not timed
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(digest, keys))
+
+    def request_step(k):
+        lr = inputs[k]
+        S = oracle.score(lr.q, sp.dtype, digests[k])
         sel = oracle.select(S, lr.rq.k)
         for b in sel.tolist():
             t_a, t_b = b * sp.bs, min((b + 1) * sp.bs, lr.rq.ctx)
@@ -263,29 +289,35 @@ def cpu_baseline(sp, inputs, B, budget_s):
         oracle.attend_f32(lr.q, lr.K, lr.V, sp.dtype, sp.bs, sel)
 
     half = budget_s / 2
+    n = len(keys)
     done, t0 = 0, time.perf_counter()
     while True:
-        request_step(done % B)
+        request_step(keys[done % n])
         done += 1
         el1 = time.perf_counter() - t0
         if el1 >= half:
             break
     single = 1.0 / (el1 / done * B)
-    threads = max(1, min(16, os.cpu_count() or 1))
     n_thr, t0 = 0, time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         while True:  # rounds of one request per thread
-            list(ex.map(request_step, [(n_thr + i) % B for i in range(threads)]))
+            list(ex.map(request_step, [keys[(n_thr + i) % n] for i in range(threads)]))
             n_thr += threads
             el2 = time.perf_counter() - t0
             if el2 >= half:
                 break
+
+    def seen(m):
+        return f"all {n}" if m >= n else f"the first {m} of {n}"
+
+    layers = sorted({k[0] for k in keys})
+    where = f"layer {layers[0]}" if len(layers) == 1 else f"layers {layers}"
     return {"value": 1.0 / (el2 / n_thr * B), "unit": "layer-steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{n_thr} request-steps of layer 0 on {threads} threads ({el2:.1f} s), "
-                      f"scaled to a {B}-request layer-step",
+            "sample": f"{n_thr} request-steps of {where} on {threads} threads ({el2:.1f} s, "
+                      f"{seen(n_thr)} slices), scaled to a {B}-request layer-step",
             "single_thread": {"value": single, "cores": 1,
-                              "sample": f"{done} request-steps ({el1:.1f} s)"},
+                              "sample": f"{done} request-steps ({el1:.1f} s, {seen(done)} slices)"},
             **host_cpu()}
 
 
@@ -803,11 +835,284 @@ def decode32_report(args):
     print(json.dumps(res), flush=True)
 
 
+def attend_read_bytes(sp, reqs, rec_bytes):
+    """Bytes the attention must read: the selected records and the queries."""
+    return sum(min(rq.k, rq.nb) for rq in reqs) * rec_bytes + len(reqs) * sp.Hq * sp.d * sp.es
+
+
+def score_read_bytes(sp, reqs, sets=1):
+    """Bytes the score kernel must move: digests and queries read, fp64
+    scores written."""
+    nb_tot = sum(rq.nb for rq in reqs)
+    return nb_tot * sp.Hkv * sp.d * 4 + len(reqs) * sp.Hq * sp.d * sp.es + nb_tot * sets * 8
+
+
+def kernel_rate(ms, nbytes):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"avg_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes, "hbm_gbps": round(gbps, 1),
+            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def recall_engines(case, layer, mode, with_pool, n=10):
+    """Recall of one layer with each engine: wall clock around n calls after
+    a stats call and two untimed ones (stream synchronised before and after),
+    transfers and mean transfer size from the stats."""
+    topk = [rq.k for rq in case.reqs]
+    bufs = H.make_buffers(case, mode)
+    kv.kvoff_select(case.ctx, layer, case.rids, case.q[layer], case.digest[layer], case.nb_max,
+                    topk, mode, bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+    out = {}
+    for engine, ename in ((kv.KVOFF_ENGINE_ZEROCOPY, "zerocopy"), (kv.KVOFF_ENGINE_DMA, "dma"),
+                          (kv.KVOFF_ENGINE_STAGED, "staged")):
+        def rec(stats=False):
+            return kv.kvoff_recall(case.ctx, layer, case.rids, mode, bufs.sel_idx, bufs.sel_cnt,
+                                   case.k_stride, case.pool_hit.get(layer) if with_pool else None,
+                                   case.pool_slot.get(layer) if with_pool else None, case.nb_max,
+                                   case.pool, case.n_slots, case.recall_base[0], bufs.table, engine,
+                                   want_stats=stats)
+        st = rec(True)
+        rec()
+        rec()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(n):
+            rec()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t) * 1e3 / n
+        out[ename] = {"ms": round(ms, 4), "gbps": round(st["bytes"] / (ms * 1e-3) / 1e9, 2),
+                      "bytes": st["bytes"], "transfers": st["transfers"],
+                      "mean_transfer_kib": round(st["bytes"] / max(1, st["transfers"]) / 1024, 2)}
+    return out
+
+
+def co_runner(case, layer, mode):
+    """What each recall engine costs a kernel running beside it: a fixed
+    HBM-bound kernel (kvoff_probe_read over a 1 GiB device buffer, 2048
+    workgroups) timed alone, then a batch of the same reads on a second
+    stream with one recall issued right behind it on the recall stream (the
+    batch lasts about three recalls, so the recall runs inside it).  Reports
+    the reads' HBM rate alone and beside each engine, and each recall's own
+    rate alone and with the reads beside it."""
+    topk = [rq.k for rq in case.reqs]
+    bufs = H.make_buffers(case, mode)
+    kv.kvoff_select(case.ctx, layer, case.rids, case.q[layer], case.digest[layer], case.nb_max,
+                    topk, mode, bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    rs, ps = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def reads(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(ps)
+        for _ in range(n):
+            kv.kvoff_probe_read(buf, nbytes, sink, 2048, stream=ps)
+        e1.record(ps)
+        return e0, e1
+
+    def recall(engine, stats=False):
+        return kv.kvoff_recall(case.ctx, layer, case.rids, mode, bufs.sel_idx, bufs.sel_cnt,
+                               case.k_stride, None, None, 0, case.pool, case.n_slots,
+                               case.recall_base[0], bufs.table, engine, want_stats=stats,
+                               stream=rs)
+
+    torch.cuda.synchronize()
+    e0, e1 = reads(3)
+    e0, e1 = reads(20)
+    torch.cuda.synchronize()
+    read_ms = e0.elapsed_time(e1) / 20
+    res = {"kernel": "kvoff_probe_read: 1 GiB of HBM, 2048 workgroups",
+           "alone_gbps": round(nbytes / (read_ms * 1e-3) / 1e9, 1), "engines": {}}
+    for engine, ename in ((kv.KVOFF_ENGINE_ZEROCOPY, "zerocopy"), (kv.KVOFF_ENGINE_DMA, "dma"),
+                          (kv.KVOFF_ENGINE_STAGED, "staged")):
+        st = recall(engine, True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        recall(engine)
+        torch.cuda.synchronize()
+        alone = (time.perf_counter() - t) * 1e3
+        n = max(4, int(math.ceil(3 * alone / read_ms)))
+        e0, e1 = reads(n)
+        t = time.perf_counter()
+        recall(engine)
+        rs.synchronize()
+        beside = (time.perf_counter() - t) * 1e3
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        res["engines"][ename] = {
+            "reads_beside_gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "reads_slowdown": round(ms / read_ms, 3),
+            "recall_alone_gbps": round(st["bytes"] / (alone * 1e-3) / 1e9, 2),
+            "recall_beside_reads_gbps": round(st["bytes"] / (beside * 1e-3) / 1e9, 2)}
+    del buf
+    return res
+
+
+# Layers each extra workload rotates through (tiny and headwise-vs-SoloHead:
+# 4, as the headline, so no step finds its digests in the MALL; the 32-layer
+# step: all 32; variable recall: one 9 GB layer, whose 272 MiB of digests
+# exceed the MALL by themselves).
+CONFIG_LAYERS = {1: 4, 3: 32, 4: 1, 5: 4}
+
+
+def measure_config(num, args, link_peak):
+    """One workload's entry of the configs object: layer-steps/s through
+    kvoff_step, recall GB/s against the measured link peak, score and
+    attention kernel HBM rates from events bound to each dispatch, and the
+    oracle's baseline on host cores."""
+    L = CONFIG_LAYERS[num]
+    sp = synth.spec(num, L=L)
+    reqs = synth.request_draws(sp)
+    B = len(reqs)
+    layers = list(range(L))
+    pool = sp.pool_frac > 0
+    want_cpu = not args.no_cpu_baseline
+    t0 = time.time()
+    log(f"[config {num}] generating and offloading {L} layers x {B} requests of '{sp.name}'")
+    case = H.build_case(sp, lambda key: synth.gen_layer_request(sp, key[0], key[1], reqs[key[1]]),
+                        layers, reqs, keep=lambda l, r: want_cpu and l == 0, with_pool_hits=pool)
+    log(f"[config {num}] set up in {time.time() - t0:.1f} s")
+    mode, engine = kv.KVOFF_SOLOHEAD, kv.KVOFF_ENGINE_ZEROCOPY
+    topk = [rq.k for rq in reqs]
+    scale = 1.0 / math.sqrt(sp.d)
+    stream = torch.cuda.current_stream()
+    sets = [H.make_buffers(case, mode) for _ in range(2)]
+    bufs = sets[0]
+    rec_bytes = kv.kvoff_record_bytes(case.ctx)
+
+    def serial(l, evs=None):
+        if evs:
+            evs[0].record(stream)
+        kv.kvoff_select(case.ctx, l, case.rids, case.q[l], case.digest[l], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        kv.kvoff_recall(case.ctx, l, case.rids, mode, bufs.sel_idx, bufs.sel_cnt, case.k_stride,
+                        case.pool_hit.get(l) if pool else None,
+                        case.pool_slot.get(l) if pool else None, case.nb_max, case.pool,
+                        case.n_slots, case.recall_base[0], bufs.table, engine, stream=stream)
+        if evs:
+            evs[2].record(stream)
+        kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[l], case.pool, case.n_slots,
+                               bufs.table, bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale,
+                               bufs.out, bufs.ws, stream=stream)
+        if evs:
+            evs[3].record(stream)
+
+    n_serial = L * max(1, -(-args.steps // L))
+    for i in range(min(args.warmup, n_serial)):
+        serial(layers[i % L])
+    torch.cuda.synchronize()
+    # per-layer recalled bytes (pool hits are not moved)
+    rec_by_layer = {}
+    for l in layers:
+        kv.kvoff_select(case.ctx, l, case.rids, case.q[l], case.digest[l], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride)
+        st = kv.kvoff_recall(case.ctx, l, case.rids, mode, bufs.sel_idx, bufs.sel_cnt,
+                             case.k_stride, case.pool_hit.get(l) if pool else None,
+                             case.pool_slot.get(l) if pool else None, case.nb_max, case.pool,
+                             case.n_slots, case.recall_base[0], bufs.table, engine, want_stats=True)
+        rec_by_layer[l] = st
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_serial)]
+    t = time.perf_counter()
+    for i in range(n_serial):
+        serial(layers[i % L], ev[i])
+    torch.cuda.synchronize()
+    serial_ms = (time.perf_counter() - t) * 1e3 / n_serial
+    rec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    rec_gbps = float(np.mean([rec_by_layer[layers[i % L]]["bytes"] / (rec_ms[i] * 1e-3) / 1e9
+                              for i in range(n_serial)]))
+    kv.kvoff_set_kernel_timing(case.ctx, True)
+    for i in range(n_serial):
+        serial(layers[i % L])
+    km = kv.kvoff_get_kernel_times(case.ctx)
+    kv.kvoff_set_kernel_timing(case.ctx, False)
+    outs = [torch.empty_like(bufs.out) for _ in layers]
+    copy = torch.cuda.Stream()
+
+    def step(n_layers=L):
+        return kv.kvoff_step(
+            case.ctx, layer_begin=0, layer_end=n_layers, req_ids=case.rids, topk=topk, mode=mode,
+            engine=engine, k_stride=case.k_stride, q=[case.q[l] for l in layers],
+            digest=[case.digest[l] for l in layers], digest_stride=case.nb_max,
+            slot_pool=case.pool, n_slots=case.n_slots, recall_base_slot=case.recall_base,
+            scores=[b.scores for b in sets], sel_idx=[b.sel_idx for b in sets],
+            sel_cnt=[b.sel_cnt for b in sets], block_table=[b.table for b in sets], scale=scale,
+            out=outs, ws=bufs.ws, pool_hit=[case.pool_hit[l] for l in layers] if pool else None,
+            pool_slot=[case.pool_slot[l] for l in layers] if pool else None,
+            pool_stride=case.nb_max, compute_stream=stream, copy_stream=copy)
+
+    n_calls = max(3, args.steps // 4) if L == 32 else max(1, -(-args.steps // L))
+    step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(n_calls):
+        step()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t) * 1e3 / (n_calls * L)
+    per_step_bytes = float(np.mean([rec_by_layer[l]["bytes"] for l in layers]))
+    entry = {
+        "workload": f"{sp.name}: batch {B}, {sp.Hq}/{sp.Hkv} heads, head_dim {sp.d}, "
+                    + (f"contexts {min(rq.ctx for rq in reqs)}-{max(rq.ctx for rq in reqs)}, "
+                       f"top-k {min(topk)}-{max(topk)} blocks"
+                       if sp.ctx_range else f"context {reqs[0].ctx}, top-{reqs[0].k}")
+                    + f", block {sp.bs}, {'bf16' if sp.dtype == synth.BF16 else 'fp16'}"
+                    + (f", {int(sp.pool_frac * 100)}% of blocks resident in the HBM pool"
+                       if pool else "")
+                    + (", one full decode step of 32 layers" if L == 32
+                       else f", {L} rotating layers" if L > 1 else ", one layer"),
+        "layer_steps_per_s": round(1e3 / step_ms, 3),
+        "ms_per_layer_step": round(step_ms, 4),
+        "schedule": f"kvoff_step over the {L} layers, {n_calls} calls: recall of layer l+1 on "
+                    "two copy streams under select/attention of layer l" if L > 1
+                    else f"kvoff_step over the one layer, {n_calls} calls",
+        "serial_one_stream": {"layer_steps_per_s": round(1e3 / serial_ms, 3),
+                              "ms_per_layer_step": round(serial_ms, 4)},
+        "recall": {"bytes_per_layer_step": int(per_step_bytes), "gbps": round(rec_gbps, 2),
+                   "frac_of_measured_link_peak": round(rec_gbps / link_peak, 4),
+                   "how": f"events around each recall, {n_serial} layer-steps in serial order"},
+        "kernels": {"score_kernel": kernel_rate(km["score_ms"], score_read_bytes(sp, reqs)),
+                    "topk_kernel": {"avg_us": round(km["topk_ms"] * 1e3, 2)},
+                    "attend_kernel": kernel_rate(km["attend_ms"],
+                                                 attend_read_bytes(sp, reqs, rec_bytes)),
+                    "combine_kernel": {"avg_us": round(km["combine_ms"] * 1e3, 2)},
+                    "bytes": "score: digests and queries read, scores written; attention: "
+                             "selected records and queries read",
+                    "how": f"events bound to each dispatch, mean of {n_serial} serial layer-steps"},
+    }
+    if L == 32:
+        entry["decode_step_ms"] = round(step_ms * L, 3)
+        entry["recall"]["in_kvoff_step_gbps"] = round(per_step_bytes / (step_ms * 1e-3) / 1e9, 2)
+    if pool:
+        st = rec_by_layer[0]
+        entry["recall"]["pool_hits"] = st["pool_hits"]
+        entry["fragmentation"] = {
+            "solohead": recall_engines(case, 0, kv.KVOFF_SOLOHEAD, True),
+            "headwise": recall_engines(case, 0, kv.KVOFF_HEADWISE, True),
+            "how": "layer 0 with its pool hits, wall clock around 10 recalls per engine"}
+    if num == 4:
+        entry["recall_engines"] = recall_engines(case, 0, mode, False)
+    if want_cpu:
+        log(f"[config {num}] timing the oracle on host cores")
+        cpu = cpu_baseline(sp, case.inputs, B, args.config_cpu_seconds,
+                           keys=[(0, r) for r in range(B)])
+        if L == 32:
+            cpu["decode_step_s"] = round(L / cpu["value"], 3)
+            cpu["single_thread"]["decode_step_s"] = round(L / cpu["single_thread"]["value"], 3)
+            cpu["sample"] += "; a 32-layer decode step is 32 such layer-steps"
+        entry["cpu_baseline"] = cpu
+    H.destroy(case)
+    del case, sets, bufs, outs
+    torch.cuda.empty_cache()
+    log(f"[config {num}] {entry['layer_steps_per_s']} layer-steps/s in {time.time() - t0:.1f} s")
+    return entry
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by request with no exchange; see the design notes)",
+              "(the path shards by request with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -899,6 +1204,31 @@ def main():
     kern_ms = kv.kvoff_get_kernel_times(case.ctx)
     kv.kvoff_set_kernel_timing(case.ctx, False)
     assert kern_ms["select_calls"] == kern_ms["decode_calls"] == args.steps, kern_ms
+    # 1c) the same kernels with their inputs in HBM only: a 1 GiB read of an
+    #     unrelated buffer before each select and each attention evicts the
+    #     256 MB MALL (the reads are not inside the kernels' events)
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4096, dtype=torch.uint8, device="cuda")
+
+    def one_step_clean(i):
+        l = layers[i % len(layers)]
+        kv.kvoff_probe_read(flush, flush.numel(), sink, 2048, stream=stream)
+        kv.kvoff_select(case.ctx, l, case.rids, case.q[l], case.digest[l], case.nb_max, topk, mode,
+                        bufs.scores, bufs.sel_idx, bufs.sel_cnt, case.k_stride, stream=stream)
+        kv.kvoff_recall(case.ctx, l, case.rids, mode, bufs.sel_idx, bufs.sel_cnt, case.k_stride,
+                        None, None, 0, case.pool, case.n_slots, case.recall_base[0], bufs.table,
+                        engine, stream=stream)
+        kv.kvoff_probe_read(flush, flush.numel(), sink, 2048, stream=stream)
+        kv.kvoff_sparse_decode(case.ctx, case.rids, mode, case.q[l], case.pool, case.n_slots,
+                               bufs.table, bufs.sel_idx, bufs.sel_cnt, case.k_stride, scale,
+                               bufs.out, bufs.ws, stream=stream)
+
+    kv.kvoff_set_kernel_timing(case.ctx, True)
+    for i in range(args.steps):
+        one_step_clean(args.warmup + i)
+    kern_clean = kv.kvoff_get_kernel_times(case.ctx)
+    kv.kvoff_set_kernel_timing(case.ctx, False)
+    del flush
 
     # 2) the headline: kvoff_step over the rotating layers, recall of layer
     #    l+1 on the copy streams under select/attention of layer l; one call
@@ -1034,6 +1364,10 @@ def main():
             if engine == kv.KVOFF_ENGINE_ZEROCOPY else None,
             "traffic_note": "counter bytes per launch: host-link fetches + HBM writes "
                             "(a copy moves each byte twice)",
+            "traffic_from": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes over this command "
+                            "with the current recall.hip (profiles/llama3-8b-layer_pmc_traffic.md), "
+                            "stored in bench.py, not counted in this run; null when recall.hip "
+                            "has changed since",
             "algorithmic_bytes": recall_bytes, "avg_ms": round(roof_ms, 4),
             "avg_ms_from": "HIP events around each recall, the layers in serial order on one stream",
             "frac_of_measured_link_peak": round(roof_gbps / link_peak, 4),
@@ -1059,10 +1393,18 @@ def main():
         "kernels": {
             "score_kernel": kernel_entry("score_ms", score_bytes),
             "topk_kernel": kernel_entry("topk_ms"),
-            "attend_kernel": kernel_entry("attend_ms", attend_kernel_bytes),
+            "attend_kernel": {**kernel_entry("attend_ms", attend_kernel_bytes),
+                              "input": "warm: the records the recall wrote just before, part of "
+                                       "them still in the 256 MB MALL (MALL-assisted, not an HBM "
+                                       "rate; clean_hbm below is)"},
             "combine_kernel": kernel_entry("combine_ms"),
             "how": f"start/stop events bound to each kernel's dispatch (kvoff_set_kernel_timing), "
                    f"serial order on one stream, mean of {args.steps} layer-steps",
+            "clean_hbm": {
+                "score_kernel": kernel_rate(kern_clean["score_ms"], score_bytes),
+                "attend_kernel": kernel_rate(kern_clean["attend_ms"], attend_kernel_bytes),
+                "how": "the same layer-steps with a 1 GiB read of an unrelated buffer before each "
+                       "select and each attention: every input byte comes from HBM"},
         },
         "serial_one_stream": {"layer_steps_per_s": round(1e3 / serial_ms, 3),
                               "ms_per_step": round(serial_ms, 4),
@@ -1077,10 +1419,30 @@ def main():
     if not args.no_overlap and graph_replay is not None:
         result["graph_replay"] = graph_replay
     result["offload_setup"] = offload_timing(case, sp, inputs, B)
+    log("recall engines and their cost to a co-running HBM kernel")
+    result["recall_engines"] = recall_engines(case, 0, mode, False)
+    result["recall_engines"]["how"] = "layer 0, wall clock around 10 recalls per engine"
+    result["co_runner"] = co_runner(case, 0, mode)
     if keep_cpu:
         log("timing the oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(sp, inputs, B, args.cpu_seconds)
     H.destroy(case)
+    del case, bufs, sets, outs, inputs
+    torch.cuda.empty_cache()
+    if args.config_list:
+        link_peak = max(copy_peak, probe_peak)
+        cfg = {"2": {"workload": result["config"]["workload"],
+                     "layer_steps_per_s": result["value"], "ms_per_layer_step": result["ms_per_step"],
+                     "schedule": result["config"]["schedule"],
+                     "recall": {"bytes_per_layer_step": recall_bytes,
+                                "gbps": result["roofline"]["achieved"],
+                                "frac_of_measured_link_peak": result["recall_frac_of_link_peak"]},
+                     "kernels": {k: result["kernels"][k] for k in ("score_kernel", "attend_kernel")},
+                     "cpu_baseline": result.get("cpu_baseline"),
+                     "note": "the headline workload: the figures of the line above"}}
+        for num in args.config_list:
+            cfg[str(num)] = measure_config(num, args, link_peak)
+        result["configs"] = dict(sorted(cfg.items()))
     print(json.dumps(result), flush=True)
 
 
