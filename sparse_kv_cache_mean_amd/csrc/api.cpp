@@ -3,6 +3,7 @@
 // in the .hip files; this file only validates and dispatches.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -25,6 +26,11 @@ int fail(int status, const char* fmt, ...) {
   vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
   va_end(ap);
   return status;
+}
+
+bool test_fail_alloc(const char* what) {
+  const char* e = std::getenv("KVOFF_TEST_FAIL_ALLOC");
+  return e && std::strcmp(e, what) == 0;
 }
 
 int make_batch(const kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, BatchIds* out) {
@@ -136,7 +142,7 @@ int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
                        (c.host_mem_kind == KVOFF_HOST_COHERENT ? hipHostMallocCoherent
                                                                : hipHostMallocNonCoherent);
       void* p = nullptr;
-      e = hipHostMalloc(&p, bytes, flags);
+      e = test_fail_alloc("store") ? hipErrorOutOfMemory : hipHostMalloc(&p, bytes, flags);
       if (e != hipSuccess || !p) {
         status = fail(KVOFF_ENOMEM, "pinned store of %zu bytes: %s", bytes, hipGetErrorString(e));
         break;
@@ -149,7 +155,10 @@ int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
         break;
       }
       ctx->store_dev = (uint8_t*)dp;
-      e = hipMalloc(&ctx->d_reqs, sizeof(ReqDev) * (size_t)c.max_requests);
+      // a device allocation that fails is a HIP error (EHIP), after the
+      // store was allocated: the teardown below frees it
+      e = test_fail_alloc("table") ? hipErrorOutOfMemory
+                                   : hipMalloc(&ctx->d_reqs, sizeof(ReqDev) * (size_t)c.max_requests);
       if (e == hipSuccess) e = hipMalloc(&ctx->d_counters, 8 * sizeof(unsigned long long));
       if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_stage, hipEventDisableTiming);
       for (int i = 0; i < 2 && e == hipSuccess; ++i)

@@ -111,6 +111,14 @@ namespace kvoff {
 void set_error(const char* fmt, ...);
 int fail(int status, const char* fmt, ...);
 
+// Test switch for the allocation-failure paths: true when the environment
+// variable KVOFF_TEST_FAIL_ALLOC names `what` ("store": the pinned store of
+// kvoff_create; "table": the device request table, allocated after the
+// store; "staging": the staged engine's pinned staging buffer).  Read at
+// each of those allocations, which are rare, so a test can set and clear it
+// between calls.
+bool test_fail_alloc(const char* what);
+
 // Runs an entry point's body and turns any C++ exception (a failed host
 // allocation, a worker thread that cannot be created) into a status code, so
 // none crosses the C ABI.

@@ -184,13 +184,14 @@ int bad_slots(int64_t n_bad, int64_t n_slots) {
               (long long)n_bad, (long long)n_slots);
 }
 
-int ensure_host(void** buf, size_t* cap, size_t need) {
+int ensure_host(void** buf, size_t* cap, size_t need, bool staging = false) {
   if (*cap >= need) return KVOFF_OK;
   if (*buf) KVOFF_HIP(hipHostFree(*buf));
   *buf = nullptr;
   *cap = 0;
   void* p = nullptr;
-  hipError_t e = hipHostMalloc(&p, need, hipHostMallocDefault);
+  hipError_t e = staging && test_fail_alloc("staging") ? hipErrorOutOfMemory
+                                                      : hipHostMalloc(&p, need, hipHostMallocDefault);
   if (e != hipSuccess) return fail(KVOFF_ENOMEM, "staging buffer of %zu bytes: %s", need, hipGetErrorString(e));
   *buf = p;
   *cap = need;
@@ -322,7 +323,7 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   // Everything this call allocates is allocated before the first copy is
   // enqueued, so a failure leaves no copy in flight that reads the staging
   // the next call rewrites.
-  if ((st = ensure_host(&ctx->stage_buf, &ctx->stage_cap, total))) return st;
+  if ((st = ensure_host(&ctx->stage_buf, &ctx->stage_cap, total, true))) return st;
   if (!ctx->stage_pool) {
     // one hardware thread is left to the issuing thread, which spins on the
     // chunk counters while the workers copy

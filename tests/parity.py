@@ -12,6 +12,9 @@ Bars:
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -152,16 +155,26 @@ def check_recall(c, l, mode, bufs, slices, with_pool_hits=False, region=0, stats
         assert stats["bytes"] == exp["items_recalled"] * item
 
 
+def oracle_attention_one(s, sl, mode):
+    """The oracle's fp32 attention of one (layer, request) slice, [Hq][d]."""
+    lr = sl.lr
+    if per_head(mode):
+        return oracle.attend_headwise_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, head_sets(sl, mode))
+    return oracle.attend_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, shared_set(sl, mode))
+
+
 def oracle_attention(c, l, mode, slices):
+    """The oracle's attention of every request of layer l, [B][Hq][d]: one
+    oracle call per request, run on a pool of threads (the calls share no
+    state and release the interpreter lock), each writing its own row."""
     s = c.s
     out = np.empty((c.B, s.Hq, s.d), np.float32)
-    for r in range(c.B):
-        sl = slices[(l, r)]
-        lr = sl.lr
-        if per_head(mode):
-            out[r] = oracle.attend_headwise_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, head_sets(sl, mode))
-        else:
-            out[r] = oracle.attend_f32(lr.q, lr.K, lr.V, s.dtype, s.bs, shared_set(sl, mode))
+
+    def one(r):
+        out[r] = oracle_attention_one(s, slices[(l, r)], mode)
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(one, range(c.B)))
     return out
 
 

@@ -278,3 +278,73 @@ def test_digests_of_keys_spanning_many_binades(bs):
             assert np.array_equal(buf, rec[b].reshape(-1)), b
     finally:
         kv.kvoff_destroy(ctx_h)
+
+
+def _vm(field="VmSize"):
+    """A field of /proc/self/status in bytes.  Pinned host memory from
+    hipHostMalloc is mapped into the process's address space (VmSize) but
+    not counted as resident (VmRSS)."""
+    with open("/proc/self/status") as f:
+        for line in f:
+            if line.startswith(field + ":"):
+                return int(line.split()[1]) * 1024
+    return -1
+
+
+def _vm_all():
+    return {k: _vm(k) >> 20 for k in ("VmSize", "VmRSS", "VmLck", "VmPin")}
+
+
+def test_allocation_failures_are_reported_and_leak_nothing(monkeypatch):
+    """Allocation failures forced through KVOFF_TEST_FAIL_ALLOC:
+    - the pinned store of kvoff_create: KVOFF_ENOMEM;
+    - the device request table, after a 1 GiB store was allocated: KVOFF_EHIP,
+      with the store freed (the process's resident memory does not keep it,
+      while a context that succeeds does hold it);
+    - the staged engine's staging buffer: KVOFF_ENOMEM with nothing enqueued,
+      and the next staged recall on the context is whole and correct."""
+    cfg = dict(num_layers=1, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+               dtype=kv.KVOFF_F16, max_requests=4, host_capacity_blocks=(1 << 30) // 16384)
+    monkeypatch.setenv("KVOFF_TEST_FAIL_ALLOC", "store")
+    with pytest.raises(kv.KvoffError) as e:
+        kv.kvoff_create(**cfg)
+    assert e.value.status == kv.KVOFF_ENOMEM, e.value
+    vm0, all0 = _vm(), _vm_all()
+    monkeypatch.setenv("KVOFF_TEST_FAIL_ALLOC", "table")
+    for _ in range(3):
+        with pytest.raises(kv.KvoffError) as e:
+            kv.kvoff_create(**cfg)
+        assert e.value.status == kv.KVOFF_EHIP, e.value
+    monkeypatch.delenv("KVOFF_TEST_FAIL_ALLOC")
+    vm1, all1 = _vm(), _vm_all()
+    ctx = kv.kvoff_create(**cfg)
+    vm2, all2 = _vm(), _vm_all()
+    kv.kvoff_destroy(ctx)
+    vm3, all3 = _vm(), _vm_all()
+    H.log(f"[alloc failures] MiB: start {all0}, after 3 failed creates {all1}, with a 1 GiB "
+          f"store {all2}, after destroying it {all3}")
+    assert vm2 - vm1 > (768 << 20), "a held store shows in the mapped address space"
+    assert vm1 - vm0 < (256 << 20), "failed creates kept their stores"
+    assert vm3 - vm1 < (256 << 20)
+
+    s = synth.spec(2, B=2, ctx=4000, k=24, hot=6)
+    c, sl = _case(s)
+    try:
+        mode = kv.KVOFF_SOLOHEAD
+        bufs = H.make_buffers(c, mode)
+        _select(c, mode, bufs)
+        bufs.table.fill_(-7)
+        monkeypatch.setenv("KVOFF_TEST_FAIL_ALLOC", "staging")
+        with pytest.raises(kv.KvoffError) as e:
+            _recall(c, mode, bufs, None, None, kv.KVOFF_ENGINE_STAGED, want_stats=False)
+        assert e.value.status == kv.KVOFF_ENOMEM, e.value
+        torch.cuda.synchronize()
+        assert bool((bufs.table == -7).all()), "a failed staged recall enqueued its table upload"
+        monkeypatch.delenv("KVOFF_TEST_FAIL_ALLOC")
+        st = _recall(c, mode, bufs, None, None, kv.KVOFF_ENGINE_STAGED, want_stats=True)
+        torch.cuda.synchronize()
+        P.check_recall(c, 0, mode, bufs, sl, stats=st, engine=kv.KVOFF_ENGINE_STAGED)
+        _decode(c, mode, bufs)
+        P.check_attention(c, 0, mode, bufs, sl)
+    finally:
+        H.destroy(c)

@@ -1,14 +1,16 @@
 """GPU parity at the workloads' full sizes, in the launch configuration
 bench.py times (same context, batch, k_stride, kernels).
 
-Digests, selections and recalled bytes are compared for every block; the
-oracle computes attention for every (request, head) row where that is cheap
-(Llama-3-8B-shaped layer) and for one sampled KV group per request elsewhere
-(its G heads, computed one group at a time by the same oracle call on that
-group's keys and values).
+Digests, selections and recalled bytes are compared for every block, and
+attention for every (request, head) row of every compared layer: all 32
+layers of the decode step, all requests and heads of the variable-recall
+layer and of the headwise-vs-SoloHead workload in each selection mode.  The
+oracle runs one call per (layer, request) on a pool of threads.
 """
 import math
+import os
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -23,33 +25,20 @@ from tests import workloads
 
 pytestmark = pytest.mark.gpu
 
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
 
 def _conditioned(s, layers, reqs, lam=None, group_lam=None):
-    sl = {}
-    for l in layers:
-        for r, rq in enumerate(reqs):
-            sl[(l, r)] = workloads.make_slice(s, l, r, rq, lam=lam, group_lam=group_lam)
-    return sl
+    """Gap-conditioned slices of every (layer, request), built on a pool of
+    threads (generation and the oracle's scoring release the interpreter
+    lock)."""
+    keys = [(l, r) for l in layers for r in range(len(reqs))]
 
+    def one(key):
+        return workloads.make_slice(s, key[0], key[1], reqs[key[1]], lam=lam, group_lam=group_lam)
 
-def _sampled_attention(c, l, mode, bufs, slices, groups):
-    """Compare the G heads of KV group groups[r] of every request r."""
-    s = c.s
-    G = s.G
-    got = bufs.out.cpu().numpy()
-    worst = (0.0, 0.0)
-    for r in range(c.B):
-        g = groups[r]
-        sl = slices[(l, r)]
-        lr = sl.lr
-        Kg = np.ascontiguousarray(lr.K[:, g:g + 1, :])
-        Vg = np.ascontiguousarray(lr.V[:, g:g + 1, :])
-        qg = lr.q[g * G:(g + 1) * G]
-        sel = P.head_sets(sl, mode)[g] if P.per_head(mode) else P.shared_set(sl, mode)
-        ref = oracle.attend_f32(qg, Kg, Vg, s.dtype, s.bs, sel)
-        err = P.check_attention_close(got[r, g * G:(g + 1) * G], ref, f"(layer {l} req {r} group {g})")
-        worst = (max(worst[0], err[0]), max(worst[1], err[1]))
-    return worst
+    with ThreadPoolExecutor(THREADS) as ex:
+        return dict(zip(keys, ex.map(one, keys)))
 
 
 def test_llama3_8b_layer_full_size():
@@ -62,30 +51,25 @@ def test_llama3_8b_layer_full_size():
     c = H.build_case(s, {k: v.lr for k, v in sl.items()}, [0], reqs, two_regions=False)
     try:
         bufs = H.make_buffers(c, kv.KVOFF_SOLOHEAD)
+        ref = P.oracle_attention(c, 0, kv.KVOFF_SOLOHEAD, sl)
         H.log("  zero-copy layer step")
         st = H.run_layer(c, 0, kv.KVOFF_SOLOHEAD, bufs, want_stats=True)
         torch.cuda.synchronize()
         P.check_digests(c, 0, sl)
         P.check_selection(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
         P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st)
-        err = P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
+        err = P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, ref)
         H.log(f"  stats {st}; attention max abs {err[0]:.2e} row rel {err[1]:.2e}")
         hot_hit = np.mean([len(set(np.flatnonzero(sl[(0, r)].lr.hot)) & set(sl[(0, r)].sel.tolist()))
                            / max(1, sl[(0, r)].lr.hot.sum()) for r in range(c.B)])
         H.log(f"  planted hot blocks recovered: {hot_hit:.3f}")
-        H.log("  DMA recall")
-        c.pool.zero_()
-        st2 = H.run_layer(c, 0, kv.KVOFF_SOLOHEAD, bufs, engine=kv.KVOFF_ENGINE_DMA, want_stats=True)
-        torch.cuda.synchronize()
-        P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st2)
-        P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
-        H.log("  staged recall")
-        c.pool.zero_()
-        st3 = H.run_layer(c, 0, kv.KVOFF_SOLOHEAD, bufs, engine=kv.KVOFF_ENGINE_STAGED,
-                          want_stats=True)
-        torch.cuda.synchronize()
-        P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st3, engine=kv.KVOFF_ENGINE_STAGED)
-        P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
+        for engine in (kv.KVOFF_ENGINE_DMA, kv.KVOFF_ENGINE_STAGED):
+            H.log(f"  engine {engine}")
+            c.pool.zero_()
+            st2 = H.run_layer(c, 0, kv.KVOFF_SOLOHEAD, bufs, engine=engine, want_stats=True)
+            torch.cuda.synchronize()
+            P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st2, engine=engine)
+            P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, ref)
     finally:
         H.destroy(c)
     H.log(f"  done in {time.time() - t0:.1f} s")
@@ -107,9 +91,11 @@ def test_variable_contexts_full_size():
         P.check_digests(c, 0, sl)
         P.check_selection(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
         P.check_recall(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, stats=st)
-        err = _sampled_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl, [r % s.Hkv for r in range(c.B)])
+        t1 = time.time()
+        err = P.check_attention(c, 0, kv.KVOFF_SOLOHEAD, bufs, sl)
         mean_run = st["items_recalled"] / st["transfers"]
-        H.log(f"  stats {st}; mean run {mean_run:.2f} blocks; attention {err}")
+        H.log(f"  stats {st}; mean run {mean_run:.2f} blocks; attention (all {c.B} x {s.Hq} rows, "
+              f"oracle {time.time() - t1:.1f} s) max abs {err[0]:.2e} row rel {err[1]:.2e}")
         assert mean_run > 2.0  # clustered hot runs were coalesced
     finally:
         H.destroy(c)
@@ -129,6 +115,7 @@ def test_headwise_vs_solohead_full_size():
     try:
         report = {}
         for mode in (kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE):
+            ref = P.oracle_attention(c, 0, mode, sl)
             for engine in (kv.KVOFF_ENGINE_ZEROCOPY, kv.KVOFF_ENGINE_DMA):
                 bufs = H.make_buffers(c, mode)
                 st = H.run_layer(c, 0, mode, bufs, engine=engine, with_pool_hits=True,
@@ -136,30 +123,34 @@ def test_headwise_vs_solohead_full_size():
                 torch.cuda.synchronize()
                 P.check_selection(c, 0, mode, bufs, sl)
                 P.check_recall(c, 0, mode, bufs, sl, with_pool_hits=True, stats=st)
-                _sampled_attention(c, 0, mode, bufs, sl, [(3 * r) % s.Hkv for r in range(c.B)])
+                err = P.check_attention(c, 0, mode, bufs, sl, ref)
                 report[(mode, engine)] = st
                 H.log(f"  mode {mode} engine {engine}: {st}, mean transfer "
-                      f"{st['bytes'] / max(1, st['transfers']) / 1024:.1f} KiB")
+                      f"{st['bytes'] / max(1, st['transfers']) / 1024:.1f} KiB, attention {err}")
         for mode in (kv.KVOFF_CONSENSUS, kv.KVOFF_CONSENSUS_GROUP):  # lambda 0.5 (default)
             bufs = H.make_buffers(c, mode)
             st = H.run_layer(c, 0, mode, bufs, with_pool_hits=True, want_stats=True)
             torch.cuda.synchronize()
             P.check_selection(c, 0, mode, bufs, sl)
             P.check_recall(c, 0, mode, bufs, sl, with_pool_hits=True, stats=st)
-            _sampled_attention(c, 0, mode, bufs, sl, [(5 * r + 1) % s.Hkv for r in range(c.B)])
-            # attention mass of two sampled requests against the oracle
+            err = P.check_attention(c, 0, mode, bufs, sl)
+            # attention mass of every request against the oracle
             mass = torch.empty((c.B, s.Hq), dtype=torch.float64, device="cuda")
             kv.kvoff_attention_mass(c.ctx, 0, c.rids, mode, c.q[0], bufs.sel_idx, bufs.sel_cnt,
                                     c.k_stride, 1.0 / math.sqrt(s.d), mass)
             torch.cuda.synchronize()
             got = mass.cpu().numpy()
-            for r in (0, c.B - 1):
+
+            def mass_ref(r):
                 x = sl[(0, r)]
                 sets = P.block_sets(x, mode)
-                ref = oracle.attention_mass(x.lr.q, x.lr.K, s.dtype, s.bs,
-                                            np.stack(sets) if len(sets) > 1 else sets[0])
-                assert np.abs(got[r] - ref).max() <= 1e-4, (mode, r)
-            H.log(f"  mode {mode}: {st}; mean mass {got.mean():.4f}")
+                return oracle.attention_mass(x.lr.q, x.lr.K, s.dtype, s.bs,
+                                             np.stack(sets) if len(sets) > 1 else sets[0])
+
+            with ThreadPoolExecutor(THREADS) as ex:
+                ref_mass = np.stack(list(ex.map(mass_ref, range(c.B))))
+            assert np.abs(got - ref_mass).max() <= 1e-4, mode
+            H.log(f"  mode {mode}: {st}; attention {err}; mean mass {got.mean():.4f}")
         solo, hw = report[(0, 0)], report[(1, 0)]
         assert hw["transfers"] > 4 * solo["transfers"]  # per-head recall fragments
         unions = [oracle.union_count(sl[(0, r)].sel_g, [sl[(0, r)].K] * s.Hkv) for r in range(c.B)]
@@ -172,25 +163,42 @@ def test_headwise_vs_solohead_full_size():
 
 def test_32_layer_step_full_size():
     """All 32 layers of the 8-request decode step offloaded (about 34 GB of
-    pinned host KV); the overlapped kvoff_step must equal the serial order bit
-    for bit on every layer, and three layers are checked against the oracle."""
+    pinned host KV).  The overlapped kvoff_step must equal the serial order
+    bit for bit on every layer and the oracle on every layer, request and
+    head; every layer's digests and selections are compared too, and three
+    layers' recalled bytes.  The inputs are generated, gap-conditioned and
+    run through the oracle one layer at a time on a pool of threads; only the
+    three byte-checked layers keep their keys and values afterwards."""
     t0 = time.time()
     s = synth.spec(3)
     reqs = synth.request_draws(s)
-    checked = (0, 15, 31)
-    H.log(f"[full llama3-8b-32layer] conditioning checked layers {checked}")
-    sl = _conditioned(s, checked, reqs)
+    B, layers = len(reqs), list(range(s.L))
+    byte_checked = (0, 15, 31)
+    sl, ref, pending = {}, {}, {}
+    mode = kv.KVOFF_SOLOHEAD
+
+    def prepare(key):
+        x = workloads.make_slice(s, key[0], key[1], reqs[key[1]])
+        return x, P.oracle_attention_one(s, x, mode)
 
     def get(key):
         l, r = key
-        return sl[key].lr if l in checked else synth.gen_layer_request(s, l, r, reqs[r])
+        if key not in pending:  # the first request of a layer: build the whole layer
+            keys = [(l, rr) for rr in range(B)]
+            with ThreadPoolExecutor(THREADS) as ex:
+                pending.update(zip(keys, ex.map(prepare, keys)))
+        x, ref[key] = pending.pop(key)
+        sl[key] = x
+        lr = x.lr
+        if l not in byte_checked:  # keep the digests and selections, drop the inputs
+            x.lr = synth.LayerRequest(lr.layer, lr.req, lr.rq, lr.q, lr.qhat, lr.hot, lr.attempts,
+                                      None, None, lr.pool)
+        return lr
 
-    H.log(f"  offloading 32 layers (built checked layers in {time.time() - t0:.1f} s)")
-    layers = list(range(s.L))
-    c = H.build_case(s, get, layers, reqs, keep=lambda l, r: l in checked)
-    H.log(f"  offloaded in {time.time() - t0:.1f} s")
+    H.log(f"[full llama3-8b-32layer] generating, conditioning and offloading 32 layers")
+    c = H.build_case(s, get, layers, reqs, keep=lambda l, r: False)
+    H.log(f"  offloaded, oracle done in {time.time() - t0:.1f} s")
     try:
-        mode = kv.KVOFF_SOLOHEAD
         sets = [H.make_buffers(c, mode) for _ in range(2)]
         outs = [torch.empty((c.B, s.Hq, s.d), dtype=torch.float32, device="cuda") for _ in layers]
         compute, copy = torch.cuda.Stream(), torch.cuda.Stream()
@@ -216,16 +224,27 @@ def test_32_layer_step_full_size():
         over = [o.cpu().numpy().copy() for o in outs]
         step(compute)
         torch.cuda.synchronize()
+        worst = (0.0, 0.0)
         for l in layers:
             assert np.array_equal(outs[l].cpu().numpy().view(np.uint32), over[l].view(np.uint32)), l
-        for l in checked:
-            P.check_attention_close(over[l], P.oracle_attention(c, l, mode, sl), f"layer {l}")
-            bufs = H.make_buffers(c, mode)
-            st = H.run_layer(c, l, mode, bufs, want_stats=True)
-            torch.cuda.synchronize()
+            want = np.stack([ref[(l, r)] for r in range(B)])
+            err = P.check_attention_close(over[l], want, f"layer {l}")
+            worst = (max(worst[0], err[0]), max(worst[1], err[1]))
             P.check_digests(c, l, sl)
-            P.check_selection(c, l, mode, bufs, sl)
-            P.check_recall(c, l, mode, bufs, sl, stats=st)
+            bufs = sets[0]
+            if l in byte_checked:
+                st = H.run_layer(c, l, mode, bufs, want_stats=True)
+                torch.cuda.synchronize()
+                P.check_selection(c, l, mode, bufs, sl)
+                P.check_recall(c, l, mode, bufs, sl, stats=st)
+            else:
+                kv.kvoff_select(c.ctx, l, c.rids, c.q[l], c.digest[l], c.nb_max,
+                                [rq.k for rq in reqs], mode, bufs.scores, bufs.sel_idx,
+                                bufs.sel_cnt, c.k_stride)
+                torch.cuda.synchronize()
+                P.check_selection(c, l, mode, bufs, sl)
+        H.log(f"  all 32 layers x {B} requests x {s.Hq} heads: max abs {worst[0]:.2e}, "
+              f"row rel {worst[1]:.2e}")
     finally:
         H.destroy(c)
     H.log(f"  done in {time.time() - t0:.1f} s")
