@@ -1,8 +1,6 @@
 // api.cpp - extern "C" entry points of kvoff.h: argument checks, the
 // context, the pinned host block store and the request table.  Kernels live
 // in the .hip files; this file only validates and dispatches.
-#include <cstdarg>
-#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -10,23 +8,6 @@
 #include "kvoff_internal.h"
 
 namespace kvoff {
-
-static thread_local char g_last_error[512] = "";
-
-void set_error(const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
-  va_end(ap);
-}
-
-int fail(int status, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
-  va_end(ap);
-  return status;
-}
 
 bool test_fail_alloc(const char* what) {
   const char* e = std::getenv("KVOFF_TEST_FAIL_ALLOC");
@@ -77,21 +58,6 @@ int kernel_timing_advance(kvoff_ctx* ctx, int slot) {
 using namespace kvoff;
 
 extern "C" {
-
-const char* kvoff_strerror(int status) {
-  switch (status) {
-    case KVOFF_OK: return "success";
-    case KVOFF_EINVAL: return "invalid argument";
-    case KVOFF_ENOMEM: return "host memory allocation failed";
-    case KVOFF_ENODEV: return "no usable GPU";
-    case KVOFF_EHIP: return "HIP runtime error";
-    case KVOFF_ERANGE: return "capacity or size exceeded";
-    case KVOFF_ESTATE: return "invalid state";
-    default: return "unknown status";
-  }
-}
-
-const char* kvoff_last_error(void) { return g_last_error; }
 
 int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
   return guarded([&]() -> int {

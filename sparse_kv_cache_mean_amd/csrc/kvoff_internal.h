@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "../../include/kvoff.h"
+#include "host_errors.h"
 
 namespace kvoff {
 
@@ -107,10 +108,6 @@ struct kvoff_ctx {
 
 namespace kvoff {
 
-// thread-local message of the last failure
-void set_error(const char* fmt, ...);
-int fail(int status, const char* fmt, ...);
-
 // Test switch for the allocation-failure paths: true when the environment
 // variable KVOFF_TEST_FAIL_ALLOC names `what` ("store": the pinned store of
 // kvoff_create; "table": the device request table, allocated after the
@@ -118,22 +115,6 @@ int fail(int status, const char* fmt, ...);
 // each of those allocations, which are rare, so a test can set and clear it
 // between calls.
 bool test_fail_alloc(const char* what);
-
-// Runs an entry point's body and turns any C++ exception (a failed host
-// allocation, a worker thread that cannot be created) into a status code, so
-// none crosses the C ABI.
-template <class F>
-int guarded(F&& body) noexcept {
-  try {
-    return body();
-  } catch (const std::bad_alloc&) {
-    return fail(KVOFF_ENOMEM, "host memory allocation failed");
-  } catch (const std::exception& e) {
-    return fail(KVOFF_ESTATE, "internal error: %s", e.what());
-  } catch (...) {
-    return fail(KVOFF_ESTATE, "internal error");
-  }
-}
 
 #define KVOFF_HIP(call)                                                            \
   do {                                                                             \
