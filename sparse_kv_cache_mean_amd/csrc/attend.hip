@@ -173,8 +173,9 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 }
 
 // G >= 8 with both contractions on the matrix cores fits 3 waves per SIMD
-// when asked (G = 8: 145 VGPRs, no spills; left to itself the compiler takes
-// 176 + 32 accumulation registers, 2 waves)
+// when asked (G = 8: 160 VGPRs, no spills; left to itself the compiler takes
+// more registers and 2 waves).  G = 4 with 32-token blocks fits 4 waves
+// unasked (120 + 8 accumulation registers).
 template <int G, int BS, bool BF16, bool MFMA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MFMA && BS == 32 && G >= 8 ? 3 : 1)))
 void attend_kernel(AttendArgs a) {
@@ -186,9 +187,9 @@ void attend_kernel(AttendArgs a) {
   // P V on the matrix cores too (32-token blocks, G >= 8): P (heads x
   // tokens) from registers as the A operand, V (tokens x dims) through LDS as
   // B.  Measured at the Llama-3-8B layer's 128 MiB: G = 16 68.9 -> 30.8 us,
-  // G = 8 32.1 -> 28.4 us, G = 4 24.5 -> 27.0 us (its 32 accumulator
-  // registers cost G = 4 a wave per SIMD, and its VALU P V is cheap), so G = 4
-  // and below keep the VALU P V.
+  // G = 8 32.1 -> 28.4 us.  At G = 4 the two forms run within noise of each
+  // other (both at 4 waves per SIMD, the MFMA one when asked for it), so G = 4
+  // and below keep the simpler VALU P V.
   constexpr bool PVM = MFMA && BS == 32 && G >= 8;
   constexpr int VS = 132;  // LDS row stride of the V tile (elements): column reads hit 4 bank groups
   __shared__ float p_s[ATT_WAVES][PVM ? 1 : BS][G];
@@ -209,7 +210,11 @@ void attend_kernel(AttendArgs a) {
   const int rg = blockIdx.x / a.S;
   const int g = rg % a.Hkv;
   const int r = rg / a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform over the wave; saying so puts the wave's block
+  // ids, table entries and record addresses in scalar registers (G = 4 with
+  // 32-token blocks then fits 128 registers: 4 waves per SIMD, not 3)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int quad = lane >> 4, col = lane & 15;
 
   const ReqDev rq = a.reqs[a.batch.id[r]];
