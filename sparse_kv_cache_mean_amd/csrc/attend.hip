@@ -206,10 +206,8 @@ void attend_kernel(AttendArgs a) {
     else return &wo_s[w][0][0];
   };
 
-  const int s = blockIdx.x % a.S;
-  const int rg = blockIdx.x / a.S;
-  const int g = rg % a.Hkv;
-  const int r = rg / a.Hkv;
+  // grid (split, KV head, request): no index waits for a kernel argument
+  const int s = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform over the wave; saying so puts the wave's block
   // ids, table entries and record addresses in scalar registers (G = 4 with
@@ -217,15 +215,23 @@ void attend_kernel(AttendArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int quad = lane >> 4, col = lane & 15;
 
-  const ReqDev rq = a.reqs[a.batch.id[r]];
-  const int cnt = min(a.sel_cnt[r], a.k_stride);
-  // a split past the request's selection has nothing to do: it writes no
-  // partial, and the combine reads only the splits that hold blocks
-  if (s * ATT_WAVES * a.bpw >= cnt) return;  // uniform over the workgroup
+  // Prologue: two memory round trips before the K/V loads go out.
+  //  1. The kernel arguments, all behind one wait (the empty asm statements
+  //     are points of use; without them the compiler reads each argument
+  //     where it is first needed and waits for each in turn).
+  //  2. The query fragments, then one vector load in which each lane fetches
+  //     one of: the wave's block ids (lanes 0-3) and table entries (4-7),
+  //     the selection count (8) and the request's token count (9+).  The
+  //     indices are clamped inside the row, since the count is not known
+  //     yet.  (Left to itself the compiler loads these with scalar loads
+  //     behind the split test below, one wait each.)
+  // The K/V loads need the table entries.  Measured at the Llama-3-8B
+  // layer from clean HBM: 0.9-1.2 us less than the chain of dependent loads.
+  const int id = a.batch.id[r];
+  asm volatile("" ::"s"(a.hw), "s"(a.Hkv), "s"(a.Hq), "s"(a.k_stride), "s"(a.bpw), "s"(a.sel_idx),
+               "s"(a.table), "s"(a.sel_cnt), "s"(a.reqs), "s"(a.q), "s"(id));
   const int64_t row = a.hw ? ((int64_t)r * a.Hkv + g) * a.k_stride : (int64_t)r * a.k_stride;
   const int i0 = (s * ATT_WAVES + wave) * a.bpw;
-  const int i1 = min(i0 + a.bpw, cnt);
-
   // MFMA: B fragments, query head g*G + col, dims m*32 + quad*8 .. +7.
   // VALU: the same dims of every head of the group.
   uint4 qf[4];
@@ -244,15 +250,35 @@ void attend_kernel(AttendArgs a) {
       for (int m = 0; m < 4; ++m) qv[h][m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
     }
   }
-  // the wave's block ids and table entries, loaded once (at most 4 blocks)
-  int blk_w[4];
+  int sel_n, n_tokens;
+  int blk_w[4], ent32[4];
+  {
+    // addresses fixed before the choice, so that it is a per-lane select
+    // and not branches
+    const int32_t* p_sel = a.sel_idx + row;
+    const int32_t* p_tab = a.table + row;
+    const int32_t* p_cnt = a.sel_cnt + r;
+    const int32_t* p_tok = &a.reqs[id].n_tokens;
+    asm volatile("" ::"s"(p_sel), "s"(p_tab), "s"(p_cnt), "s"(p_tok));
+    const int i = min(i0 + (lane & 3), a.k_stride - 1);
+    const int32_t* src = lane < 4 ? p_sel + i : lane < 8 ? p_tab + i : lane == 8 ? p_cnt : p_tok;
+    const int mv = *src;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      blk_w[k] = __builtin_amdgcn_readlane(mv, k);
+      ent32[k] = __builtin_amdgcn_readlane(mv, 4 + k);
+    }
+    sel_n = __builtin_amdgcn_readlane(mv, 8);
+    n_tokens = __builtin_amdgcn_readlane(mv, 9);
+  }
   int64_t ent_w[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int i = min(i0 + k, max(i1 - 1, 0));
-    blk_w[k] = a.sel_idx[row + i];
-    ent_w[k] = a.table[row + i];
-  }
+  for (int k = 0; k < 4; ++k) ent_w[k] = ent32[k];
+  const int cnt = min(sel_n, a.k_stride);
+  // a split past the request's selection has nothing to do: it writes no
+  // partial, and the combine reads only the splits that hold blocks
+  if (s * ATT_WAVES * a.bpw >= cnt) return;  // uniform over the workgroup
+  const int i1 = min(i0 + a.bpw, cnt);
 
   float m_run = -INFINITY, l_run = 0.f;  // MFMA: head col's running max (log2) and sum
   float mh[GV], lh[GV];                  // VALU: every head's
@@ -457,7 +483,7 @@ void attend_kernel(AttendArgs a) {
       const int64_t ent = ent_w[k];
       const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
       const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
-      const int n_valid = (int)min<int64_t>(BS, (int64_t)rq.n_tokens - (int64_t)blk * BS);
+      const int n_valid = (int)min<int64_t>(BS, (int64_t)n_tokens - (int64_t)blk * BS);
       // not a valid entry (unused, or outside the request or the pool): nothing to read
       if (ent < 0 || slice >= a.n_slices || blk < 0 || n_valid <= 0) continue;
       uint4 kf[TILES][4], vf[BS / 4];
@@ -575,9 +601,12 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, fl
 
 // blocks per wave (at most 4: the per-wave index cache); KVOFF_ATT_BPW
 // overrides the default for tuning sweeps.  Measured at the Llama-3-8B
-// layer's records (k_stride 64): G = 4 equal with 2 and 4 (24.4 us), G = 8
-// 28.0 -> 25.3 us and G = 16 30.8 -> 26.6 us with 4; short selections of
-// the latency-bound small shapes keep 2 (shorter chains per wave).
+// layer's records (k_stride 64): G = 4 from clean HBM 29.3-29.6 us with 2,
+// 28.1-28.5 with 4 (fewer waves to launch and fewer partials; with the
+// records still in the MALL the two are within run-to-run noise), G = 8
+// 28.0 -> 25.3 us and G = 16 30.8 -> 26.6 us with 4.  Selections shorter
+// than 64 blocks keep 2: the small latency-bound shapes need the shorter
+// chains per wave (batch 1, 4K context, top-32: 7.7 us with 2, 9.9 with 4).
 int attend_bpw(int32_t k_stride, int G) {
   static const int forced = [] {
     const char* e = std::getenv("KVOFF_ATT_BPW");
@@ -585,7 +614,7 @@ int attend_bpw(int32_t k_stride, int G) {
     return v >= 1 && v <= 4 ? v : 0;
   }();
   if (forced) return forced;
-  return k_stride <= 128 && G < 8 ? 2 : 4;
+  return k_stride < 64 && G < 8 ? 2 : 4;
 }
 
 template <int G, int BS, bool MFMA>
@@ -645,7 +674,7 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   a.Hkv = ctx->cfg.num_kv_heads;
   a.hw = mode == KVOFF_HEADWISE;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)(b.n * a.Hkv * a.S));
+  const dim3 grid((unsigned)a.S, (unsigned)a.Hkv, (unsigned)b.n);
   const bool bf16 = ctx->cfg.dtype == KVOFF_BF16;
   const int bs = ctx->cfg.block_size;
   const bool mfma = ctx->attn_qk == KVOFF_QK_MFMA;
