@@ -281,7 +281,7 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
       return fail(KVOFF_EINVAL, "NULL buffer argument");
     if (layout_of(mode) < 0) return fail(KVOFF_EINVAL, "mode %d", mode);
     if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
-    int64_t max_nb = 0;
+    int64_t max_nb = 0, min_nb = INT64_MAX;
     for (int i = 0; i < n_req; ++i) {
       const ReqHost& r = ctx->reqs[b.id[i]];
       if (topk[i] < 1) return fail(KVOFF_EINVAL, "topk[%d] = %d < 1", i, topk[i]);
@@ -292,10 +292,11 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
         return fail(KVOFF_EINVAL, "digest_stride %lld < nb %lld of request %d",
                     (long long)digest_stride, (long long)r.nb, i);
       if (r.nb > max_nb) max_nb = r.nb;
+      if (r.nb < min_nb) min_nb = r.nb;
     }
     KVOFF_HIP(hipSetDevice(ctx->device));
     hipStream_t s = (hipStream_t)stream;
-    st = launch_score(ctx, b, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
+    st = launch_score(ctx, b, min_nb, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
     if (st) return st;
     if ((st = kernel_timing_advance(ctx, KT_SCORE))) return st;
     // consensus selections use the layout of their scope (shared or per KV head)

@@ -37,7 +37,7 @@
 //        reads of the four quads fall in different banks) and each lane
 //        gathers its B operand column V[8q .. 8q+7][dim]; one MFMA pair per
 //        16-dim chunk accumulates o[head][dim] with no cross-quad sum.  At
-//        G = 4 the VALU form is faster: it keeps 3 waves per SIMD.
+//        G = 4 the two forms measure the same, and the VALU one stays.
 // The four waves merge in LDS; one partial (m, l, o[128]) per (head, split)
 // goes to the workspace and combine_kernel merges the splits in fixed split
 // order, so results are deterministic.  (Merging in the last-arriving
@@ -219,37 +219,21 @@ void attend_kernel(AttendArgs a) {
   //  1. The kernel arguments, all behind one wait (the empty asm statements
   //     are points of use; without them the compiler reads each argument
   //     where it is first needed and waits for each in turn).
-  //  2. The query fragments, then one vector load in which each lane fetches
-  //     one of: the wave's block ids (lanes 0-3) and table entries (4-7),
-  //     the selection count (8) and the request's token count (9+).  The
-  //     indices are clamped inside the row, since the count is not known
-  //     yet.  (Left to itself the compiler loads these with scalar loads
-  //     behind the split test below, one wait each.)
-  // The K/V loads need the table entries.  Measured at the Llama-3-8B
-  // layer from clean HBM: 0.9-1.2 us less than the chain of dependent loads.
+  //  2. One vector load in which each lane fetches one of: the wave's block
+  //     ids (lanes 0-3) and table entries (4-7), the selection count (8) and
+  //     the request's token count (9+).  The indices are clamped inside the
+  //     row, since the count is not known yet.  (Left to itself the compiler
+  //     loads these with scalar loads behind the split test below, one wait
+  //     each.)
+  // The query fragments load after the split test, beside the K/V loads:
+  // a split with nothing to do then reads nothing more (the variable-recall
+  // layer has thousands of them).  Measured at the Llama-3-8B layer from
+  // clean HBM: 0.9-1.2 us less than the chain of dependent loads.
   const int id = a.batch.id[r];
   asm volatile("" ::"s"(a.hw), "s"(a.Hkv), "s"(a.Hq), "s"(a.k_stride), "s"(a.bpw), "s"(a.sel_idx),
                "s"(a.table), "s"(a.sel_cnt), "s"(a.reqs), "s"(a.q), "s"(id));
   const int64_t row = a.hw ? ((int64_t)r * a.Hkv + g) * a.k_stride : (int64_t)r * a.k_stride;
   const int i0 = (s * ATT_WAVES + wave) * a.bpw;
-  // MFMA: B fragments, query head g*G + col, dims m*32 + quad*8 .. +7.
-  // VALU: the same dims of every head of the group.
-  uint4 qf[4];
-  uint4 qv[GV][4];
-  if constexpr (MFMA) {
-    // columns col >= G repeat head G-1: MFMA output columns are independent
-    // and those columns' logits are never stored, so they need no zeroing
-    const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + min(col, G - 1)) * D;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) qf[m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
-  } else {
-#pragma unroll
-    for (int h = 0; h < GV; ++h) {
-      const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + h) * D;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) qv[h][m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
-    }
-  }
   int sel_n, n_tokens;
   int blk_w[4], ent32[4];
   {
@@ -279,6 +263,25 @@ void attend_kernel(AttendArgs a) {
   // partial, and the combine reads only the splits that hold blocks
   if (s * ATT_WAVES * a.bpw >= cnt) return;  // uniform over the workgroup
   const int i1 = min(i0 + a.bpw, cnt);
+
+  // MFMA: B fragments, query head g*G + col, dims m*32 + quad*8 .. +7.
+  // VALU: the same dims of every head of the group.
+  uint4 qf[4];
+  uint4 qv[GV][4];
+  if constexpr (MFMA) {
+    // columns col >= G repeat head G-1: MFMA output columns are independent
+    // and those columns' logits are never stored, so they need no zeroing
+    const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + min(col, G - 1)) * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qf[m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
+  } else {
+#pragma unroll
+    for (int h = 0; h < GV; ++h) {
+      const uint16_t* qh = a.q + ((int64_t)r * a.Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) qv[h][m] = *reinterpret_cast<const uint4*>(qh + m * 32 + quad * 8);
+    }
+  }
 
   float m_run = -INFINITY, l_run = 0.f;  // MFMA: head col's running max (log2) and sum
   float mh[GV], lh[GV];                  // VALU: every head's
@@ -561,7 +564,11 @@ void attend_kernel(AttendArgs a) {
 
 // One workgroup per (request, head), one thread per dim: single-pass merge
 // of the request's non-empty splits in order (ceil(count / blocks per
-// split) of the S), loads batched NB splits at a time.
+// split) of the S), loads batched NB splits at a time.  The first batch is
+// loaded together with the selection count rather than after it (split
+// indices clamped to S - 1, inside the request's rows): one memory round
+// trip, not two.  Splits past the count hold stale workspace bytes, which
+// are read and never used.
 template <int NB>
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, float* out, int S,
                                                           const int32_t* sel_cnt, int k_stride,
@@ -569,32 +576,39 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, fl
   const int64_t rh = blockIdx.x;  // request * Hq + head
   const int j = threadIdx.x;
   const float* P = part + rh * S * PART;
-  const int cnt = min(sel_cnt[rh / Hq], k_stride);
-  const int Sr = min(S, (cnt + per_split - 1) / per_split);
-  float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < Sr; s0 += NB) {
-    float m[NB], l[NB], o[NB];
+  const int cnt_raw = sel_cnt[rh / Hq];
+  float m[NB], l[NB], o[NB];
+  auto load = [&](int s0, int last) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const int t = min(s0 + k, Sr - 1);
+      const int t = min(s0 + k, last);
       m[k] = P[t * PART];
       l[k] = P[t * PART + 1];
       o[k] = P[t * PART + 2 + j];
     }
+  };
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  // branch-free, so that no load waits behind a test of an earlier split
+  auto merge = [&](int s0, int Sr) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (s0 + k >= Sr || m[k] == -INFINITY) continue;
-      if (m[k] > M) {
-        const float f = M == -INFINITY ? 0.f : exp2f(M - m[k]);
-        L = fmaf(L, f, l[k]);
-        O = fmaf(O, f, o[k]);
-        M = m[k];
-      } else {
-        const float f = exp2f(m[k] - M);
-        L = fmaf(l[k], f, L);
-        O = fmaf(o[k], f, O);
-      }
+      const bool use = s0 + k < Sr && m[k] != -INFINITY;
+      const float mk = use ? m[k] : -INFINITY;
+      const float Mn = fmaxf(M, mk);
+      const float fa = M == -INFINITY ? 0.f : exp2f(M - Mn);  // rescales what is merged so far
+      const float fb = use ? exp2f(mk - Mn) : 0.f;           // weighs this split
+      L = fmaf(L, fa, (use ? l[k] : 0.f) * fb);
+      O = fmaf(O, fa, (use ? o[k] : 0.f) * fb);
+      M = Mn;
     }
+  };
+  load(0, S - 1);
+  const int cnt = min(cnt_raw, k_stride);
+  const int Sr = min(S, (cnt + per_split - 1) / per_split);
+  merge(0, Sr);
+  for (int s0 = NB; s0 < Sr; s0 += NB) {
+    load(s0, Sr - 1);
+    merge(s0, Sr);
   }
   out[rh * kHeadDim + j] = L > 0.f ? O / L : 0.f;
 }

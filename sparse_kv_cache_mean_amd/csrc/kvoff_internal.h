@@ -170,9 +170,9 @@ int make_batch(const kvoff_ctx* ctx, int32_t n_req, const int32_t* req_ids, Batc
 int launch_offload(const kvoff_ctx* ctx, int32_t layer, int32_t req_id, const void* k_dev,
                    const void* v_dev, float* digest_dev, hipStream_t stream);
 
-int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t max_nb, const void* q_dev,
-                 const float* digest_dev, int64_t digest_stride, int32_t mode, double* scores_dev,
-                 hipStream_t stream);
+int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t min_nb, int64_t max_nb,
+                 const void* q_dev, const float* digest_dev, int64_t digest_stride, int32_t mode,
+                 double* scores_dev, hipStream_t stream);
 
 int launch_topk(const kvoff_ctx* ctx, const BatchIds& b, const int32_t* topk_host,
                 int32_t mode, const double* scores_dev, int64_t digest_stride,

@@ -59,6 +59,7 @@ struct ScoreArgs {
   const float* digest;
   double* scores;
   int64_t stride;
+  int64_t nb_lo;  // the fewest blocks of any request of the batch, at launch
   int32_t Hq, Hkv, G, bf16;
   double lambda;  // consensus mode only
 };
@@ -107,9 +108,19 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   __shared__ double u_s[NC * 256];
   extern __shared__ uint4 q_s[];  // the request's q rows, Hq * 16 chunks of 16 bytes
   const int r = blockIdx.y;
-  const ReqDev rq = a.reqs[a.batch.id[r]];
   const int64_t b0 = (int64_t)blockIdx.x * SCORE_WG_BLOCKS;
-  if (b0 >= rq.nb) return;  // uniform over the workgroup
+  // A workgroup whose blocks all lie below the batch's shortest request
+  // issues its digest loads at once; only the others first wait for their
+  // request's block count (and leave if they hold no block of it).  The
+  // count stands in for the request's own one: every block test below is
+  // against it, and all of this workgroup's blocks pass.
+  int64_t nb;
+  if (b0 + SCORE_WG_BLOCKS <= a.nb_lo) {
+    nb = b0 + SCORE_WG_BLOCKS;
+  } else {
+    nb = a.reqs[a.batch.id[r]].nb;
+    if (b0 >= nb) return;  // uniform over the workgroup
+  }
   const int F = a.Hkv * kHeadDim;
   const int tid = threadIdx.x;
 
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   float4 v[SCORE_BPW][NC];
 #pragma unroll
   for (int k = 0; k < SCORE_BPW; ++k) {
-    const int64_t b = min<int64_t>(bw + k, rq.nb - 1);
+    const int64_t b = min<int64_t>(bw + k, nb - 1);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int idx = min(c * 256 + lane * 4, F - 4);
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
           sm += xor_move(sm, 1 << st);
         }
         const int gw = (c * 256 + (lane & 32) * 4) / kHeadDim;  // the half's KV head
-        if ((lane & 31) == 0 && b < rq.nb && gw < a.Hkv)
+        if ((lane & 31) == 0 && b < nb && gw < a.Hkv)
           a.scores[((int64_t)r * a.Hkv + gw) * a.stride + b] = mx + a.lambda * (sm / (double)GG);
       }
     }
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       }
       acc = sum32(acc);
       acc += __shfl_xor(acc, 32);
-      if (lane == 0 && b < rq.nb) a.scores[(int64_t)r * a.stride + b] = acc;
+      if (lane == 0 && b < nb) a.scores[(int64_t)r * a.stride + b] = acc;
     } else {
       // per-KV-head sums: a KV head's 128 dims are 32 consecutive lanes of
       // one chunk, so chunk c holds heads 2c (lanes 0-31) and 2c+1 (32-63).
@@ -296,7 +307,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       for (int st = LN; st < 5; ++st) sg += xor_move(sg, 1 << st);
       const int g = 2 * c + (lane >> 5);  // this lane's KV head
       if constexpr (MODE == MODE_HEADWISE) {
-        if ((lane & 31) < NC && b < rq.nb && g < a.Hkv)
+        if ((lane & 31) < NC && b < nb && g < a.Hkv)
           a.scores[((int64_t)r * a.Hkv + g) * a.stride + b] = sg;
       } else {
         // consensus: S = max_g S_g + lambda * mean_g S_g over the KV heads
@@ -308,7 +319,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         }
         mx = fmax(mx, __shfl_xor(mx, 32));
         sm += __shfl_xor(sm, 32);
-        if (lane == 0 && b < rq.nb) a.scores[(int64_t)r * a.stride + b] = mx + a.lambda * (sm / (double)a.Hkv);
+        if (lane == 0 && b < nb) a.scores[(int64_t)r * a.stride + b] = mx + a.lambda * (sm / (double)a.Hkv);
       }
     }
   }
@@ -469,9 +480,12 @@ __global__ __launch_bounds__(256) void topk_regs_kernel(TopkArgs a) {
   const int K = a.k[r] < nb ? a.k[r] : nb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  // the keys load together with the block count, not after it: indices are
+  // clamped inside the row (stride entries); keys past the count are never
+  // counted or taken
   uint64_t keys[KPT];
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) keys[k] = score_key(S[min(tid + 256 * k, nb - 1)]);
+  for (int k = 0; k < KPT; ++k) keys[k] = score_key(S[min<int64_t>(tid + 256 * k, a.stride - 1)]);
 
   hist[0][tid] = 0;
   __syncthreads();
@@ -616,9 +630,9 @@ void score_launch(const ScoreArgs& a, int64_t max_nb, int mode, hipStream_t s, K
 
 }  // namespace
 
-int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t max_nb, const void* q_dev,
-                 const float* digest_dev, int64_t digest_stride, int32_t mode, double* scores_dev,
-                 hipStream_t stream) {
+int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t min_nb, int64_t max_nb,
+                 const void* q_dev, const float* digest_dev, int64_t digest_stride, int32_t mode,
+                 double* scores_dev, hipStream_t stream) {
   ScoreArgs a;
   a.batch = b;
   a.reqs = ctx->d_reqs;
@@ -626,6 +640,7 @@ int launch_score(const kvoff_ctx* ctx, const BatchIds& b, int64_t max_nb, const 
   a.digest = digest_dev;
   a.scores = scores_dev;
   a.stride = digest_stride;
+  a.nb_lo = min_nb;
   a.Hq = ctx->cfg.num_q_heads;
   a.Hkv = ctx->cfg.num_kv_heads;
   a.G = ctx->G;
