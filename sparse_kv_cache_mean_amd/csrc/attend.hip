@@ -83,6 +83,7 @@ int attend_scratch_address(int device, void** out) {
 namespace {
 
 constexpr int ATT_WAVES = 4;
+constexpr int MAXB = 8;  // most blocks per wave
 constexpr int PART = 2 + kHeadDim;  // m, l, o[128]
 
 
@@ -220,11 +221,12 @@ void attend_kernel(AttendArgs a) {
   //     are points of use; without them the compiler reads each argument
   //     where it is first needed and waits for each in turn).
   //  2. One vector load in which each lane fetches one of: the wave's block
-  //     ids (lanes 0-3) and table entries (4-7), the selection count (8) and
-  //     the request's token count (9+).  The indices are clamped inside the
-  //     row, since the count is not known yet.  (Left to itself the compiler
-  //     loads these with scalar loads behind the split test below, one wait
-  //     each.)
+  //     ids (lanes 0-7) and table entries (8-15), the selection count (16)
+  //     and the request's token count (17+).  The indices are clamped inside
+  //     the row, since the count is not known yet.  The value stays in its
+  //     register, and each block's id and entry are read from it with a
+  //     scalar lane select.  (Left to itself the compiler loads these with
+  //     scalar loads behind the split test below, one wait each.)
   // The query fragments load after the split test, beside the K/V loads:
   // a split with nothing to do then reads nothing more (the variable-recall
   // layer has thousands of them).  Measured at the Llama-3-8B layer from
@@ -234,8 +236,7 @@ void attend_kernel(AttendArgs a) {
                "s"(a.table), "s"(a.sel_cnt), "s"(a.reqs), "s"(a.q), "s"(id));
   const int64_t row = a.hw ? ((int64_t)r * a.Hkv + g) * a.k_stride : (int64_t)r * a.k_stride;
   const int i0 = (s * ATT_WAVES + wave) * a.bpw;
-  int sel_n, n_tokens;
-  int blk_w[4], ent32[4];
+  int sel_n, n_tokens, mv;
   {
     // addresses fixed before the choice, so that it is a per-lane select
     // and not branches
@@ -244,20 +245,15 @@ void attend_kernel(AttendArgs a) {
     const int32_t* p_cnt = a.sel_cnt + r;
     const int32_t* p_tok = &a.reqs[id].n_tokens;
     asm volatile("" ::"s"(p_sel), "s"(p_tab), "s"(p_cnt), "s"(p_tok));
-    const int i = min(i0 + (lane & 3), a.k_stride - 1);
-    const int32_t* src = lane < 4 ? p_sel + i : lane < 8 ? p_tab + i : lane == 8 ? p_cnt : p_tok;
-    const int mv = *src;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      blk_w[k] = __builtin_amdgcn_readlane(mv, k);
-      ent32[k] = __builtin_amdgcn_readlane(mv, 4 + k);
-    }
-    sel_n = __builtin_amdgcn_readlane(mv, 8);
-    n_tokens = __builtin_amdgcn_readlane(mv, 9);
+    const int i = min(i0 + (lane & (MAXB - 1)), a.k_stride - 1);
+    const int32_t* src = lane < MAXB       ? p_sel + i
+                         : lane < 2 * MAXB  ? p_tab + i
+                         : lane == 2 * MAXB ? p_cnt
+                                            : p_tok;
+    mv = *src;
+    sel_n = __builtin_amdgcn_readlane(mv, 2 * MAXB);
+    n_tokens = __builtin_amdgcn_readlane(mv, 2 * MAXB + 1);
   }
-  int64_t ent_w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ent_w[k] = ent32[k];
   const int cnt = min(sel_n, a.k_stride);
   // a split past the request's selection has nothing to do: it writes no
   // partial, and the combine reads only the splits that hold blocks
@@ -480,10 +476,12 @@ void attend_kernel(AttendArgs a) {
 
   {
 #pragma unroll 1
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < MAXB; ++k) {
       if (i0 + k >= i1) break;
-      const int blk = blk_w[k];
-      const int64_t ent = ent_w[k];
+      // block id and table entry of the wave's k-th block, from the lanes
+      // that fetched them (k is uniform: a scalar lane select)
+      const int blk = __builtin_amdgcn_readlane(mv, k);
+      const int64_t ent = __builtin_amdgcn_readlane(mv, MAXB + k);
       const int64_t slice = a.hw ? ent : ent * a.Hkv + g;
       const uint16_t* Kp = reinterpret_cast<const uint16_t*>(a.pool + slice * a.slice_bytes);
       const int n_valid = (int)min<int64_t>(BS, (int64_t)n_tokens - (int64_t)blk * BS);
@@ -613,23 +611,42 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* part, fl
   out[rh * kHeadDim + j] = L > 0.f ? O / L : 0.f;
 }
 
-// blocks per wave (at most 4: the per-wave index cache); KVOFF_ATT_BPW
-// overrides the default for tuning sweeps.  Measured at the Llama-3-8B
-// layer's records (k_stride 64): G = 4 from clean HBM 29.3-29.6 us with 2,
-// 28.1-28.5 with 4 (fewer waves to launch and fewer partials; with the
-// records still in the MALL the two are within run-to-run noise), G = 8
-// 28.0 -> 25.3 us and G = 16 30.8 -> 26.6 us with 4.  Selections shorter
-// than 64 blocks keep 2: the small latency-bound shapes need the shorter
-// chains per wave (batch 1, 4K context, top-32: 7.7 us with 2, 9.9 with 4).
-int attend_bpw(int32_t k_stride, int G) {
+// Selected blocks per wave (at most MAXB); KVOFF_ATT_BPW overrides the
+// default for tuning sweeps.  Fewer, longer workgroups launch faster and
+// leave fewer split partials, as long as the grid still covers the 256
+// compute units.  Measured, attention / combine from clean HBM:
+//   Llama-3-8B layer (G = 4, k 64): 2 blocks 29.3-29.6 us, 4 27.7-28.1,
+//     8 27.1-27.4 (256 workgroups);
+//   variable-recall layer (G = 8, k up to 572): 4 blocks 190 / 12.7 us,
+//     8 186.5-186.9 / 10.5-10.6 us;
+//   the same shapes at batch 8: 8 blocks leave 128 workgroups, 24.4-24.8
+//     against 16.8 us with 4;
+//   batch 1, 4K context, top-32 (latency-bound): 2 blocks 7.7 us, 4 9.9.
+int attend_bpw(int32_t n_req, int32_t Hkv, int32_t k_stride, int G) {
   static const int forced = [] {
     const char* e = std::getenv("KVOFF_ATT_BPW");
     const int v = e ? std::atoi(e) : 0;
-    return v >= 1 && v <= 4 ? v : 0;
+    return v >= 1 && v <= MAXB ? v : 0;
   }();
   if (forced) return forced;
-  return k_stride < 64 && G < 8 ? 2 : 4;
+  if (k_stride < 64) return G < 8 ? 2 : 4;
+  const int64_t wg8 = (int64_t)n_req * Hkv * ((k_stride + ATT_WAVES * 8 - 1) / (ATT_WAVES * 8));
+  return wg8 >= 256 ? 8 : 4;
 }
+
+}  // namespace
+
+int attend_splits(int32_t n_req, int32_t Hkv, int32_t k_stride, int G) {
+  const int per = ATT_WAVES * attend_bpw(n_req, Hkv, k_stride, G);
+  return (k_stride + per - 1) / per;
+}
+
+size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride) {
+  return (size_t)n_req * ctx->cfg.num_q_heads *
+         attend_splits(n_req, ctx->cfg.num_kv_heads, k_stride, ctx->G) * PART * sizeof(float);
+}
+
+namespace {
 
 template <int G, int BS, bool MFMA>
 void launch_g_bs_qk(const AttendArgs& a, bool bf16, dim3 grid, hipStream_t s, KEv ev) {
@@ -657,15 +674,6 @@ void launch_g(const AttendArgs& a, int bs, bool bf16, bool mfma, dim3 grid, hipS
 
 }  // namespace
 
-int attend_splits(int32_t k_stride, int G) {
-  const int per = ATT_WAVES * attend_bpw(k_stride, G);
-  return (k_stride + per - 1) / per;
-}
-
-size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride) {
-  return (size_t)n_req * ctx->cfg.num_q_heads * attend_splits(k_stride, ctx->G) * PART * sizeof(float);
-}
-
 int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,
                   const void* pool, int64_t n_slots, const int32_t* table, const int32_t* sel_idx,
                   const int32_t* sel_cnt, int32_t k_stride, float scale, float* out, void* ws,
@@ -682,8 +690,8 @@ int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const v
   a.slice_bytes = ctx->slice_bytes;
   a.n_slices = n_slots * ctx->cfg.num_kv_heads;
   a.k_stride = k_stride;
-  a.bpw = attend_bpw(k_stride, ctx->G);
-  a.S = attend_splits(k_stride, ctx->G);
+  a.bpw = attend_bpw(b.n, ctx->cfg.num_kv_heads, k_stride, ctx->G);
+  a.S = attend_splits(b.n, ctx->cfg.num_kv_heads, k_stride, ctx->G);
   a.Hq = ctx->cfg.num_q_heads;
   a.Hkv = ctx->cfg.num_kv_heads;
   a.hw = mode == KVOFF_HEADWISE;

@@ -217,7 +217,7 @@ int launch_mass(const kvoff_ctx* ctx, const BatchIds& b, int32_t layer, int32_t 
 int attend_scratch_address(int device, void** out);
 
 // split policy of the attention kernel: number of splits per (request, KV head)
-int attend_splits(int32_t k_stride, int G);
+int attend_splits(int32_t n_req, int32_t Hkv, int32_t k_stride, int G);
 size_t attend_ws_bytes(const kvoff_ctx* ctx, int32_t n_req, int32_t k_stride);
 
 int launch_attend(const kvoff_ctx* ctx, const BatchIds& b, int32_t mode, const void* q_dev,

@@ -312,27 +312,31 @@ def test_dtype_and_block_size_grid(dtype, bs):
         H.destroy(c)
 
 
-# 4 blocks per attention wave (selections of 64 blocks and up) at G = 4,
-# with counts that leave waves partly filled and whole splits empty: K is
-# 70, 47 (every block of a 47-block request) and 66, so the splits of 16
-# blocks end inside a wave and the short request's last two splits hold no
-# block.
-BPW4_CASES = [
+# 4 and 8 blocks per attention wave (selections of 64 blocks and up; 8 when
+# the grid still has 256 workgroups) at G = 4, with counts that leave waves
+# partly filled and whole splits empty: K is 70, 47 (every block of a
+# 47-block request) and 66, so the splits end inside a wave and the short
+# request's last split holds no block.
+BPW_CASES = [
     dict(wl=2, dtype=synth.BF16, bs=32, reqs=[(5000, 70), (1500, 70), (3000, 66)]),
     dict(wl=1, dtype=synth.F16, bs=16, reqs=[(2500, 70), (752, 70), (1500, 66)]),
+    dict(wl=2, dtype=synth.BF16, bs=32, reqs=[(3000, 70), (1500, 70), (2200, 66)] * 5 + [(1200, 70)]),
 ]
 
 
-@pytest.mark.parametrize("case", BPW4_CASES, ids=["bf16-bs32", "fp16-bs16"])
-def test_four_blocks_per_wave_with_partial_and_empty_splits(case):
-    s = synth.spec(case["wl"], B=3, dtype=case["dtype"], bs=case["bs"], ctx=5000, k=70, hot=8,
+@pytest.mark.parametrize("case", BPW_CASES, ids=["bf16-bs32-4", "fp16-bs16-4", "bf16-bs32-8"])
+def test_blocks_per_wave_with_partial_and_empty_splits(case):
+    n = len(case["reqs"])
+    s = synth.spec(case["wl"], B=n, dtype=case["dtype"], bs=case["bs"], ctx=5000, k=70, hot=8,
                    headwise=True)
     reqs = [synth.Request(ctx=ctx, nb=-(-ctx // s.bs), k=k) for ctx, k in case["reqs"]]
-    H.log(f"[bpw4] dtype {case['dtype']} bs {case['bs']} requests {case['reqs']}")
+    H.log(f"[blocks per wave] dtype {case['dtype']} bs {case['bs']} {n} requests")
     c, sl = _case(s, [0], reqs=reqs)
     try:
         assert c.k_stride == 70 and s.Hq // s.Hkv == 4
-        assert min(min(rq.k, rq.nb) for rq in reqs) <= 48  # a request with empty splits
+        assert min(min(rq.k, rq.nb) for rq in reqs) <= 48  # a request with an empty split
+        # 8 blocks per wave when 8-block splits still give 256 workgroups
+        assert (n * s.Hkv * 3 >= 256) == (n == 16)
         for mode in (kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE):
             _, err = _full_check(c, sl, 0, mode, kv.KVOFF_ENGINE_ZEROCOPY)
             H.log(f"  mode {mode} attention err {err}")

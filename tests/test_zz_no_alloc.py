@@ -81,23 +81,24 @@ def test_noalloc_decode_matches_workspace_decode(mode):
 
 
 def test_noalloc_decode_rejects_partials_past_the_array():
-    """4 requests x 32 heads x 256 splits (k_stride 4096) of 520-byte
-    partials is 17.0 MB, past the 16 MiB array: ERANGE before any launch."""
+    """8 requests x 32 heads x 128 splits (k_stride 4096, 8 blocks per wave)
+    of 520-byte partials is 17.0 MB, past the 16 MiB array: ERANGE before
+    any launch."""
     s = synth.spec(2, B=1, ctx=2048, k=8, hot=2)
     reqs = synth.request_draws(s)
     c = H.build_case(s, lambda key: synth.gen_layer_request(s, key[0], key[1], reqs[key[1]]), [0],
                      reqs)
     try:
-        k_stride = 4096
-        need = kv.kvoff_workspace_size(c.ctx, kv.KVOFF_CALL_SPARSE_DECODE, 4, k_stride,
+        k_stride, n = 4096, 8
+        need = kv.kvoff_workspace_size(c.ctx, kv.KVOFF_CALL_SPARSE_DECODE, n, k_stride,
                                        kv.KVOFF_SOLOHEAD)
         assert need > kv.KVOFF_NOALLOC_SCRATCH_BYTES, need
-        sel = torch.zeros((4, k_stride), dtype=torch.int32, device="cuda")
-        cnt = torch.zeros((4,), dtype=torch.int32, device="cuda")
-        out = torch.empty((4, s.Hq, s.d), dtype=torch.float32, device="cuda")
-        ids = [c.rids[0]] * 4
+        sel = torch.zeros((n, k_stride), dtype=torch.int32, device="cuda")
+        cnt = torch.zeros((n,), dtype=torch.int32, device="cuda")
+        out = torch.empty((n, s.Hq, s.d), dtype=torch.float32, device="cuda")
+        ids = [c.rids[0]] * n
         with pytest.raises(kv.KvoffError) as e:
-            kv.kvoff_sparse_decode_noalloc(c.ctx, ids, kv.KVOFF_SOLOHEAD, c.q[0].repeat(4, 1, 1),
+            kv.kvoff_sparse_decode_noalloc(c.ctx, ids, kv.KVOFF_SOLOHEAD, c.q[0].repeat(n, 1, 1),
                                            c.pool, c.n_slots, sel, sel, cnt, k_stride, 0.1, out)
         assert e.value.status == kv.KVOFF_ERANGE
     finally:
