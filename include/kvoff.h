@@ -108,10 +108,12 @@ enum {
      recalled item of the call (in request, [KV head,] rank order) goes to
      slot recall_base_slot + n (headwise: slice recall_base_slot*Hkv + n);
      the block table says where.  Synchronises the stream first and returns
-     once every chunk is gathered and its copy enqueued; the staging buffer
-     (pinned, grown on demand) is reused once the previous call's copies
-     completed.  The context's worker threads (one fewer than the hardware
-     threads, at most 15) spin for 500 us after a call before they sleep. */
+     once every chunk is gathered and its copy enqueued.  The context keeps
+     two sets of pinned staging buffers (grown on demand) and uses them by
+     turns: a set is reused once the copies of the call that used it last
+     have completed.  The context's worker threads (three fewer than the
+     hardware threads, at most 10) spin for 500 us after a call before they
+     sleep. */
   KVOFF_ENGINE_STAGED = 2
 };
 

@@ -126,7 +126,8 @@ int kvoff_create(const kvoff_config* cfg, kvoff_ctx** out) {
       e = test_fail_alloc("table") ? hipErrorOutOfMemory
                                    : hipMalloc(&ctx->d_reqs, sizeof(ReqDev) * (size_t)c.max_requests);
       if (e == hipSuccess) e = hipMalloc(&ctx->d_counters, 8 * sizeof(unsigned long long));
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_stage, hipEventDisableTiming);
+      for (int i = 0; i < 2 && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&ctx->stage[i].done, hipEventDisableTiming);
       for (int i = 0; i < 2 && e == hipSuccess; ++i)
         e = hipEventCreateWithFlags(&ctx->ev_sel[i], hipEventDisableTiming);
       if (e != hipSuccess) {
@@ -164,10 +165,12 @@ int kvoff_destroy(kvoff_ctx* ctx) {
     }
     for (hipEvent_t e : ctx->kt_ev)
       if (e) (void)hipEventDestroy(e);
-    if (ctx->ev_stage) (void)hipEventDestroy(ctx->ev_stage);
-    if (ctx->stage_buf) (void)hipHostFree(ctx->stage_buf);
-    if (ctx->table_host) (void)hipHostFree(ctx->table_host);
-    if (ctx->sel_host) (void)hipHostFree(ctx->sel_host);
+    for (StageSet& ss : ctx->stage) {
+      if (ss.done) (void)hipEventDestroy(ss.done);
+      if (ss.buf) (void)hipHostFree(ss.buf);
+      if (ss.table) (void)hipHostFree(ss.table);
+      if (ss.sel) (void)hipHostFree(ss.sel);
+    }
     if (ctx->d_counters) (void)hipFree(ctx->d_counters);
     if (ctx->d_reqs) (void)hipFree(ctx->d_reqs);
     if (ctx->store) (void)hipHostFree(ctx->store);

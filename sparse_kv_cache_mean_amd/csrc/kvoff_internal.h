@@ -49,6 +49,21 @@ struct ReqHost {
 
 class StagePool;
 
+// One set of the staged engine's pinned host buffers and the event behind
+// the last copy that reads them.  The context holds two, used by turns, so
+// that a call can gather into one set while the previous call's copies
+// still read the other.
+struct StageSet {
+  void* buf = nullptr;    // staging buffer, grown on demand
+  size_t cap = 0;
+  void* table = nullptr;  // block-table staging
+  size_t table_cap = 0;
+  void* sel = nullptr;    // read-back of the selection and pool maps
+  size_t sel_cap = 0;
+  hipEvent_t done = nullptr;  // behind the set's last copy
+  bool pending = false;       // `done` recorded and not yet waited for
+};
+
 // kernels timed by kvoff_set_kernel_timing, in kvoff_kernel_times order,
 // and the event sets each keeps in its ring
 enum KernelSlot { KT_SCORE = 0, KT_TOPK, KT_ATTEND, KT_COMBINE, KT_N };
@@ -80,20 +95,14 @@ struct kvoff_ctx {
   hipEvent_t ev_sel[2] = {nullptr, nullptr};  // selection -> recall hand-off per buffer set
   // staged (CPU gather + bulk copy) recall engine
   kvoff::StagePool* stage_pool = nullptr;  // host worker threads, created on first use
-  void* stage_buf = nullptr;                // pinned staging buffer, grown on demand
-  size_t stage_cap = 0;
-  void* table_host = nullptr;               // pinned block-table staging
-  size_t table_cap = 0;
-  void* sel_host = nullptr;                 // pinned read-back of the selection and pool maps
-  size_t sel_cap = 0;
-  hipEvent_t ev_stage = nullptr;            // behind the last staged copy
+  kvoff::StageSet stage[2];                 // pinned buffers, used by turns
+  int stage_next = 0;                       // the set the next staged call uses
   std::vector<hipEvent_t> ev_group;         // per request group (interruptible step)
   std::vector<hipEvent_t> ev_timing;        // timing events of kvoff_step (on request)
   void* noalloc_scratch = nullptr;          // device address of the attention scratch array
   hipStream_t copy2 = nullptr;              // kvoff_step's own second copy stream (lazy)
   hipStream_t dma_stream[kvoff::kDmaSideStreams] = {};  // DMA engine's copy streams (lazy)
   hipEvent_t dma_done[kvoff::kDmaSideStreams] = {};     // behind each one's last copy
-  bool ev_stage_pending = false;
   // per-kernel timing (kvoff_set_kernel_timing): per kernel slot a ring of
   // KT_RING (start, stop) event pairs, [slot][set][start|stop]; sets in use
   // are the `pending` ones before `next`; their durations, once read, go to

@@ -12,10 +12,19 @@
 //    order, at the start of the recall region and the block table points at
 //    them (item n of the call -> slot recall_base + n; headwise: slice
 //    recall_base*Hkv + n), so the attention reads them where they land.
-// The staging buffer and the block-table staging are reused by the next
-// call only after an event recorded behind this call's last copy (the table
-// upload when nothing is recalled) has completed; the next call may run on
-// another stream, so the event, not stream order, protects them.
+// The context keeps two sets of pinned buffers (staging, block-table
+// staging, selection read-back) and the calls use them by turns.  A set is
+// reused only after an event recorded behind its last copy has completed;
+// the next call may run on another stream, so the event, not stream order,
+// protects it.  With two sets a call gathers while the previous call's copies
+// still run (when the two calls are on different streams, as kvoff_step's
+// consecutive layers are), so the link does not wait for the read-back, the
+// plan and the first chunk.  Measured on the Llama-3-8B-shaped layer in
+// kvoff_step: 384-388 layer-steps/s with one set, 411-413 with two.
+// Optionally (KVOFF_STAGE_STREAMS=2) a call's odd chunks go to a copy stream
+// of the context, so that one copy's start overlaps the previous one's end:
+// alone, a recall then runs at 53.7-53.9 GB/s instead of 52.2-52.7, but
+// kvoff_step loses 3 layer-steps/s, so one stream is the default.
 #include <emmintrin.h>
 
 #include <algorithm>
@@ -48,6 +57,40 @@ size_t stage_chunk() {
     return v >= 4 && v <= 64 ? (size_t)v << 20 : kStageChunk;
   }();
   return c;
+}
+
+// sets of staging buffers used by turns, and streams the chunk copies of a
+// call alternate over (measured defaults; KVOFF_STAGE_SETS and
+// KVOFF_STAGE_STREAMS, 1 or 2 each, override them for tuning)
+int stage_env(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  const int v = e ? std::atoi(e) : 0;
+  return v == 1 || v == 2 ? v : dflt;
+}
+int stage_sets() {
+  static const int n = stage_env("KVOFF_STAGE_SETS", 2);
+  return n;
+}
+int stage_streams() {
+  static const int n = stage_env("KVOFF_STAGE_STREAMS", 1);
+  return n;
+}
+
+// worker threads of the pool: at most 10, and three hardware threads left
+// beside them (the issuing thread, which spins on the chunk counters while
+// the workers copy, and the HIP runtime's own threads).  Measured on 16
+// hardware threads, kvoff_step on the Llama-3-8B-shaped layer: 6 workers
+// 408-411 layer-steps/s, 10 412-413, 15 (all but the issuing thread) 332-402
+// and erratic.  KVOFF_STAGE_THREADS (1..64) overrides the count for tuning.
+int stage_threads() {
+  static const int n = [] {
+    const char* e = std::getenv("KVOFF_STAGE_THREADS");
+    const int v = e ? std::atoi(e) : 0;
+    if (v >= 1 && v <= 64) return v;
+    const int hc = (int)std::thread::hardware_concurrency();
+    return std::max(1, std::min(10, (hc > 0 ? hc : 4) - 3));
+  }();
+  return n;
 }
 
 void stage_pool_destroy(kvoff_ctx* ctx) {
@@ -90,6 +133,17 @@ struct Piece {  // one contiguous source range of the store
 
 // the call's status once its work is enqueued: ESTATE when pool hits named
 // slots outside the pool (their table entries are -1)
+// the context's first copy stream beside the caller's (shared with the DMA
+// engine; created on first use, non-blocking, default priority) and the
+// event recorded behind its last copy
+int side_stream(kvoff_ctx* ctx, hipStream_t* s, hipEvent_t* done) {
+  if (!ctx->dma_done[0]) KVOFF_HIP(hipEventCreateWithFlags(&ctx->dma_done[0], hipEventDisableTiming));
+  if (!ctx->dma_stream[0]) KVOFF_HIP(hipStreamCreateWithFlags(&ctx->dma_stream[0], hipStreamNonBlocking));
+  *s = ctx->dma_stream[0];
+  *done = ctx->dma_done[0];
+  return KVOFF_OK;
+}
+
 int bad_slots(int64_t n_bad, int64_t n_slots) {
   if (!n_bad) return KVOFF_OK;
   return fail(KVOFF_ESTATE, "%lld pool hits name a slot outside [0, %lld): table entries -1",
@@ -120,19 +174,29 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   const size_t n_sel = (size_t)b.n * sets * r.k_stride;
   const int64_t item = hw ? ctx->slice_bytes : ctx->rec_bytes;
 
-  // the previous staged call's copies must be done before its buffers are reused
-  if (ctx->ev_stage_pending) {
-    KVOFF_HIP(hipEventSynchronize(ctx->ev_stage));
-    ctx->ev_stage_pending = false;
+  // this call's set: the copies of the call that used it last must be done
+  // before its buffers are rewritten
+  const int set = stage_sets() > 1 ? ctx->stage_next : 0;
+  StageSet& ss = ctx->stage[set];
+  if (ss.pending) {
+    KVOFF_HIP(hipEventSynchronize(ss.done));
+    ss.pending = false;
   }
+  // once this call's work is enqueued: the set's event, and the other set next
+  auto enqueued = [&]() -> int {
+    KVOFF_HIP(hipEventRecord(ss.done, stream));
+    ss.pending = true;
+    ctx->stage_next = set ^ 1;
+    return KVOFF_OK;
+  };
   // read the selection (and the pool maps) back into pinned memory
   const size_t n_map = r.pool_hit || r.pool_slot ? (size_t)b.n * r.pool_stride : 0;
   const size_t o_sel = ((size_t)b.n * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t o_slot = (o_sel + n_sel * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t o_hit = (o_slot + (r.pool_slot ? n_map * sizeof(int32_t) : 0) + 255) & ~(size_t)255;
-  int st = ensure_host(&ctx->sel_host, &ctx->sel_cap, o_hit + (r.pool_hit ? n_map : 0) + 1);
+  int st = ensure_host(&ss.sel, &ss.sel_cap, o_hit + (r.pool_hit ? n_map : 0) + 1);
   if (st) return st;
-  uint8_t* rb = (uint8_t*)ctx->sel_host;
+  uint8_t* rb = (uint8_t*)ss.sel;
   const int32_t* cnt = (const int32_t*)rb;
   const int32_t* sel = (const int32_t*)(rb + o_sel);
   const int32_t* pslot = (const int32_t*)(rb + o_slot);
@@ -148,9 +212,9 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
 
   // plan: compact order of the missing items, their block-table entries and
   // the source pieces (consecutive blocks of one request coalesced)
-  st = ensure_host(&ctx->table_host, &ctx->table_cap, n_sel * sizeof(int32_t));
+  st = ensure_host(&ss.table, &ss.table_cap, n_sel * sizeof(int32_t));
   if (st) return st;
-  int32_t* table = (int32_t*)ctx->table_host;
+  int32_t* table = (int32_t*)ss.table;
   std::vector<Piece> pieces;
   int64_t n_items = 0, n_hits = 0, n_selected = 0, n_bad = 0;
   for (int ri = 0; ri < b.n; ++ri) {
@@ -191,10 +255,8 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   const size_t total = (size_t)n_items * item;
   if (total == 0) {
     KVOFF_HIP(hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream));
-    // the upload reads the block-table staging: the next call (possibly on
-    // another stream) waits for this event before rewriting it
-    KVOFF_HIP(hipEventRecord(ctx->ev_stage, stream));
-    ctx->ev_stage_pending = true;
+    // the upload reads the block-table staging: the set's event covers it
+    if ((st = enqueued())) return st;
     if (stats) {
       KVOFF_HIP(hipStreamSynchronize(stream));
       *stats = kvoff_stats{n_selected, n_hits, 0, 0, 0};
@@ -232,17 +294,19 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
   for (size_t t = 0; t < job->n; ++t) job->left[job->chunk_of[t]].fetch_add(1, std::memory_order_relaxed);
   std::vector<size_t> piece_off(pieces.size() + 1, 0);
   for (size_t i = 0; i < pieces.size(); ++i) piece_off[i + 1] = piece_off[i] + pieces[i].bytes;
-  // Everything this call allocates is allocated before the first copy is
-  // enqueued, so a failure leaves no copy in flight that reads the staging
+  // Everything this call allocates or creates is done before the first copy
+  // is enqueued, so a failure leaves no copy in flight that reads the staging
   // the next call rewrites.
-  if ((st = ensure_host(&ctx->stage_buf, &ctx->stage_cap, total, true))) return st;
-  if (!ctx->stage_pool) {
-    // one hardware thread is left to the issuing thread, which spins on the
-    // chunk counters while the workers copy
-    const unsigned hc = std::thread::hardware_concurrency();
-    ctx->stage_pool = new StagePool((int)std::max(1u, std::min(15u, (hc ? hc : 4u) - 1)));
-  }
-  uint8_t* stage = (uint8_t*)ctx->stage_buf;
+  if ((st = ensure_host(&ss.buf, &ss.cap, total, true))) return st;
+  // odd chunks go to a copy stream of the context: every earlier command of
+  // `stream` has completed (the read-back waited for them), so it may start
+  // at once, and `stream` waits for its last copy below
+  hipStream_t side = nullptr;
+  hipEvent_t side_done = nullptr;
+  const bool two = stage_streams() > 1 && n_chunks > 1;
+  if (two && (st = side_stream(ctx, &side, &side_done))) return st;
+  if (!ctx->stage_pool) ctx->stage_pool = new StagePool(stage_threads());
+  uint8_t* stage = (uint8_t*)ss.buf;
   const Piece* pc = pieces.data();
   const size_t* po = piece_off.data();
   const size_t* tl = task_lo.data();
@@ -258,7 +322,6 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
       copy_streaming(stage + a, pc[i].src + (a - po[i]), b - a);
     }
   };
-  KVOFF_HIP(hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream));
   ctx->stage_pool->run(job);
   // issue each chunk's copy as soon as it is filled, in order; every chunk
   // is waited for, also after an error, so no task outlives this call
@@ -270,17 +333,29 @@ int recall_staged(kvoff_ctx* ctx, const BatchIds& b, const RecallArgs& r, kvoff_
     const size_t o = chunk_lo[c];
     const size_t n = chunk_lo[c + 1] - o;
     if (err == KVOFF_OK) {
-      hipError_t e = hipMemcpyAsync(dst0 + o, stage + o, n, hipMemcpyHostToDevice, stream);
+      hipError_t e = hipMemcpyAsync(dst0 + o, stage + o, n, hipMemcpyHostToDevice,
+                                    two && (c & 1) ? side : stream);
       if (e != hipSuccess) err = fail(KVOFF_EHIP, "staged copy: %s", hipGetErrorString(e));
       ++n_transfers;
     }
   }
+  // the block table last: the first chunk does not wait for its upload
+  if (err == KVOFF_OK) {
+    hipError_t e = hipMemcpyAsync(r.table, table, n_sel * sizeof(int32_t), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) err = fail(KVOFF_EHIP, "block-table upload: %s", hipGetErrorString(e));
+  }
+  if (two && err == KVOFF_OK) {
+    hipError_t e = hipEventRecord(side_done, side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side_done, 0);
+    if (e != hipSuccess) err = fail(KVOFF_EHIP, "copy-stream join: %s", hipGetErrorString(e));
+  }
   if (err) {
+    // nothing may still read this set's buffers when the call returns
+    if (two) (void)hipStreamSynchronize(side);
     (void)hipStreamSynchronize(stream);
     return err;
   }
-  KVOFF_HIP(hipEventRecord(ctx->ev_stage, stream));
-  ctx->ev_stage_pending = true;
+  if ((st = enqueued())) return st;
   if (stats) {
     KVOFF_HIP(hipStreamSynchronize(stream));
     *stats = kvoff_stats{n_selected, n_hits, n_items, n_transfers, n_items * item};
