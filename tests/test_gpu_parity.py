@@ -841,6 +841,73 @@ def test_staged_recall_back_to_back_calls(mode):
         H.destroy(c)
 
 
+@pytest.mark.parametrize("mode", [kv.KVOFF_SOLOHEAD, kv.KVOFF_HEADWISE])
+def test_staged_recall_overlapping_calls(mode):
+    """Staged recalls issued on two streams with nothing waited for in
+    between: each call reads back its selection and gathers while the
+    previous call's copies are still in flight on the other stream, so the
+    engine's two staging sets alternate under load, and one of them grows
+    (a one-request call, then a three-request one, on the same set) while
+    the other set's copies run.  Every call writes its own pool region and
+    block table; all are checked byte for byte once both streams are done."""
+    s = synth.spec(2, B=4, L=2, ctx=8192, headwise=True)
+    H.log(f"[staged overlapping calls] mode {mode}")
+    c, sl = _case(s, [0, 1])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    subsets = [[0, 1, 2, 3], [2], [1, 3], [0], [3, 2, 1, 0], [0, 2, 3], [1]]
+    n_calls = 14
+    rec = kv.kvoff_record_bytes(c.ctx)
+    hw = P.per_head(mode)
+    item = rec // s.Hkv if hw else rec
+    sets = s.Hkv if hw else 1
+    region = 4 * c.k_stride  # slots of one call's recall region (at most 4 requests)
+    n_slots = n_calls * region
+    pool = torch.zeros(n_slots * rec, dtype=torch.uint8, device="cuda")
+    calls = []
+    for call in range(n_calls):
+        sub = subsets[call % len(subsets)]
+        l = call % 2
+        idx = torch.tensor(sub, device="cuda")
+        calls.append(dict(
+            sub=sub, l=l, st=streams[call % 2], base=call * region,
+            q=c.q[l].index_select(0, idx).contiguous(),
+            dg=c.digest[l].index_select(0, idx).contiguous(),
+            scores=torch.empty((len(sub), sets, c.nb_max), dtype=torch.float64, device="cuda"),
+            sel=torch.empty((len(sub), sets, c.k_stride), dtype=torch.int32, device="cuda"),
+            cnt=torch.empty((len(sub),), dtype=torch.int32, device="cuda"),
+            table=torch.full((len(sub), sets, c.k_stride), -7, dtype=torch.int32, device="cuda")))
+    torch.cuda.synchronize()
+    try:
+        for k in calls:
+            rids = [c.rids[r] for r in k["sub"]]
+            topk = [c.reqs[r].k for r in k["sub"]]
+            kv.kvoff_select(c.ctx, k["l"], rids, k["q"], k["dg"], c.nb_max, topk, mode, k["scores"],
+                            k["sel"], k["cnt"], c.k_stride, stream=k["st"])
+            kv.kvoff_recall(c.ctx, k["l"], rids, mode, k["sel"], k["cnt"], c.k_stride, None, None, 0,
+                            pool, n_slots, k["base"], k["table"], kv.KVOFF_ENGINE_STAGED,
+                            stream=k["st"])
+        torch.cuda.synchronize()
+        pool_h = pool.cpu().numpy()
+        for call, k in enumerate(calls):
+            tab = k["table"].cpu().numpy()
+            base = k["base"] * s.Hkv if hw else k["base"]
+            n = 0
+            for i, r in enumerate(k["sub"]):
+                for g, bset in enumerate(P.block_sets(sl[(k["l"], r)], mode)):
+                    want = workloads.block_records(sl[(k["l"], r)], bset.tolist())
+                    for j in range(len(bset)):
+                        ent = int(tab[i, g, j])
+                        assert ent == base + n, (call, r, g, j, ent)
+                        n += 1
+                        got = pool_h[ent * item:(ent + 1) * item]
+                        exp = (want[j, g] if hw else want[j]).reshape(-1).view(np.uint8)
+                        assert np.array_equal(got, exp), (call, r, g, j)
+                    assert (tab[i, g, len(bset):] == -1).all(), (call, r, g)
+        H.log(f"  {n_calls} calls checked")
+    finally:
+        H.destroy(c)
+
+
 @pytest.mark.parametrize("dtype", [synth.F16, synth.BF16])
 @pytest.mark.parametrize("Hq", [64, 128])
 def test_attention_pv_on_matrix_cores(dtype, Hq):
