@@ -232,7 +232,8 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
 
 /* Recall the selected blocks of one layer into the HBM slot pool.
  *   slot_pool_dev [n_slots] records of kvoff_record_bytes() each, in HBM
- *                 (the pool holds n_slots records; owned by the caller)
+ *                 (the pool holds n_slots records; owned by the caller;
+ *                 1 <= n_slots and n_slots * Hkv <= INT32_MAX)
  *   recall_base_slot  first slot of the recall region: the record of rank i
  *                 of request r goes to slot recall_base_slot + r*k_stride + i
  *                 (headwise: KV head g's slice of that slot), so consecutive
@@ -254,8 +255,9 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
  *                 unused entries -1
  *   engine        KVOFF_ENGINE_ZEROCOPY, KVOFF_ENGINE_DMA or KVOFF_ENGINE_STAGED
  *   stats         nullable; when given, filled after synchronising the stream
- * Errors: EINVAL, ERANGE (recall region past n_slots), ESTATE (layer of a
- * request not offloaded, or pool hits outside the pool as above), EHIP. */
+ * Errors: EINVAL (including n_slots outside its range), ERANGE (recall
+ * region past n_slots), ESTATE (layer of a request not offloaded, or pool
+ * hits outside the pool as above), EHIP. */
 int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* req_ids,
                  int32_t mode, const int32_t* sel_idx_dev, const int32_t* sel_cnt_dev,
                  int32_t k_stride, const uint8_t* pool_hit_dev, const int32_t* pool_slot_dev,
@@ -465,6 +467,7 @@ int kvoff_admission_plan(const kvoff_admission_policy* p, int32_t num_layers, do
  * first_slot + b for b < nb (the request's row of the maps kvoff_recall
  * takes).  Enqueued on `stream`: the caller orders later recalls after it
  * (same stream or an event) and keeps the slots out of every recall region.
+ * n_slots * Hkv must not exceed INT32_MAX.
  * Errors: EINVAL, ERANGE (slots past n_slots), ESTATE (layer not offloaded),
  * EHIP. */
 int kvoff_make_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, void* slot_pool_dev,

@@ -36,6 +36,10 @@ int kvoff_make_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, void* slo
     if (!ctx->offloaded[(size_t)req_id * ctx->cfg.num_layers + layer])
       return fail(KVOFF_ESTATE, "layer %d of request %d was not offloaded", layer, req_id);
     const ReqHost& r = ctx->reqs[req_id];
+    // pool_slot_dev entries are int32, and recall turns them into table
+    // entries (headwise: slot * Hkv + g)
+    if (n_slots > INT32_MAX / ctx->cfg.num_kv_heads)
+      return fail(KVOFF_EINVAL, "n_slots %lld > %d", (long long)n_slots, INT32_MAX / ctx->cfg.num_kv_heads);
     if (first_slot < 0 || first_slot + r.nb > n_slots)
       return fail(KVOFF_ERANGE, "slots [%lld, %lld) outside the pool's %lld", (long long)first_slot,
                   (long long)(first_slot + r.nb), (long long)n_slots);

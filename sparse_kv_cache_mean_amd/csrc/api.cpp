@@ -371,6 +371,10 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
     mode = layout_of(mode);  // consensus modes use the layout of their scope
     if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
     if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
+    // table entries are int32 slot (headwise: slice) indices
+    if (n_slots < 1 || n_slots > INT32_MAX / ctx->cfg.num_kv_heads)
+      return fail(KVOFF_EINVAL, "n_slots %lld outside [1, %d]", (long long)n_slots,
+                  INT32_MAX / ctx->cfg.num_kv_heads);
     if ((pool_hit_dev == nullptr) != (pool_slot_dev == nullptr))
       return fail(KVOFF_EINVAL, "pool_hit_dev and pool_slot_dev must both be given or both NULL");
     if (pool_hit_dev) {

@@ -626,6 +626,18 @@ def test_error_paths_on_device():
                             c.k_stride, None, None, 0, c.pool, c.n_slots, c.n_slots,
                             bufs.table)
         assert e.value.status == kv.KVOFF_ERANGE
+        # a pool whose slot (headwise: slice) indices would not fit the int32
+        # table and pool-slot entries
+        too_many = (2**31 - 1) // s.Hkv + 1
+        with pytest.raises(kv.KvoffError) as e:
+            kv.kvoff_recall(c.ctx, 0, c.rids, kv.KVOFF_SOLOHEAD, bufs.sel_idx, bufs.sel_cnt,
+                            c.k_stride, None, None, 0, c.pool, too_many, 0, bufs.table)
+        assert e.value.status == kv.KVOFF_EINVAL
+        hit = torch.zeros(c.nb_max, dtype=torch.uint8, device="cuda")
+        slot = torch.zeros(c.nb_max, dtype=torch.int32, device="cuda")
+        with pytest.raises(kv.KvoffError) as e:
+            kv.kvoff_make_resident(c.ctx, 0, c.rids[0], c.pool, too_many, 0, hit, slot)
+        assert e.value.status == kv.KVOFF_EINVAL
         with pytest.raises(kv.KvoffError) as e:  # workspace too small
             kv.kvoff_sparse_decode(c.ctx, c.rids, kv.KVOFF_SOLOHEAD, c.q[0], c.pool, c.n_slots, bufs.table,
                                    bufs.sel_idx, bufs.sel_cnt, c.k_stride, 0.1, bufs.out,
