@@ -36,8 +36,12 @@
  *     values passed as void* (NULL = the null stream).
  *   - Calls enqueue work and return; outputs are valid once the stream has
  *     synchronised.  Exceptions: kvoff_register_request and kvoff_create are
- *     synchronous; kvoff_recall with KVOFF_ENGINE_DMA and any call given a
- *     non-NULL kvoff_stats synchronise the stream they run on.
+ *     synchronous; kvoff_recall with KVOFF_ENGINE_DMA or KVOFF_ENGINE_STAGED
+ *     and any call given a non-NULL kvoff_stats synchronise the stream they
+ *     run on.
+ *   - A context belongs to the device that is current when kvoff_create
+ *     runs.  Every call on it runs on that device and leaves the calling
+ *     thread's current device as it found it.
  *   - Dtype of q, K, V: IEEE fp16 or bf16 (the context's dtype).
  *     head_dim must be 128; block_size 16 or 32 tokens.
  *   - Non-finite inputs give undefined results (not scanned).

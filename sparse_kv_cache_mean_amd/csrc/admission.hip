@@ -44,7 +44,8 @@ int kvoff_make_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, void* slo
       return fail(KVOFF_ERANGE, "slots [%lld, %lld) outside the pool's %lld", (long long)first_slot,
                   (long long)(first_slot + r.nb), (long long)n_slots);
     hipStream_t s = (hipStream_t)stream;
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     const uint8_t* src = ctx->store + (size_t)(r.rec_base + (int64_t)layer * r.nb) * ctx->rec_bytes;
     uint8_t* dst = (uint8_t*)slot_pool_dev + (size_t)first_slot * ctx->rec_bytes;
     KVOFF_HIP(hipMemcpyAsync(dst, src, (size_t)r.nb * ctx->rec_bytes, hipMemcpyHostToDevice, s));
@@ -64,7 +65,8 @@ int kvoff_release_resident(kvoff_ctx* ctx, int32_t layer, int32_t req_id, uint8_
       return fail(KVOFF_ESTATE, "request id %d is not registered", req_id);
     if (layer < 0 || layer >= ctx->cfg.num_layers) return fail(KVOFF_ERANGE, "layer %d", layer);
     const ReqHost& r = ctx->reqs[req_id];
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     hipLaunchKernelGGL(fill_maps_kernel, dim3((unsigned)((r.nb + 255) / 256)), dim3(256), 0,
                        (hipStream_t)stream, pool_hit_dev, (int32_t*)nullptr, (int64_t)r.nb,
                        (int64_t)0, (uint8_t)0);

@@ -218,7 +218,8 @@ int kvoff_register_request(kvoff_ctx* ctx, int64_t n_tokens, int32_t* req_id) {
     ReqHost h{ctx->store_used, n_tokens, nb};
     ReqDev d{h.rec_base, (int32_t)n_tokens, (int32_t)nb};
     int32_t id = (int32_t)ctx->reqs.size();
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     KVOFF_HIP(hipMemcpy(ctx->d_reqs + id, &d, sizeof d, hipMemcpyHostToDevice));
     ctx->reqs.push_back(h);
     ctx->offloaded.resize(ctx->reqs.size() * (size_t)ctx->cfg.num_layers, 0);
@@ -252,7 +253,8 @@ int kvoff_offload_blocks(kvoff_ctx* ctx, int32_t layer, int32_t req_id, const vo
       return fail(KVOFF_ERANGE, "layer %d outside [0, %d)", layer, ctx->cfg.num_layers);
     if (req_id < 0 || req_id >= (int32_t)ctx->reqs.size())
       return fail(KVOFF_ESTATE, "request id %d is not registered", req_id);
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     int st = launch_offload(ctx, layer, req_id, k_dev, v_dev, digest_dev, (hipStream_t)stream);
     if (st == KVOFF_OK) ctx->offloaded[(size_t)req_id * ctx->cfg.num_layers + layer] = 1;
     return st;
@@ -297,7 +299,8 @@ int kvoff_select(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
       if (r.nb > max_nb) max_nb = r.nb;
       if (r.nb < min_nb) min_nb = r.nb;
     }
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     hipStream_t s = (hipStream_t)stream;
     st = launch_score(ctx, b, min_nb, max_nb, q_dev, digest_dev, digest_stride, mode, scores_dev, s);
     if (st) return st;
@@ -382,7 +385,8 @@ int kvoff_recall(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int32_t* re
         if (ctx->reqs[b.id[i]].nb > pool_stride)
           return fail(KVOFF_EINVAL, "pool_stride %lld < nb of request %d", (long long)pool_stride, i);
     }
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     RecallArgs a{layer,       mode,         sel_idx_dev, sel_cnt_dev,
                  k_stride,    pool_hit_dev, pool_slot_dev, pool_stride,
                  (uint8_t*)slot_pool_dev, n_slots, recall_base_slot, block_table_dev};
@@ -428,7 +432,8 @@ static int sparse_decode_impl(kvoff_ctx* ctx, int32_t n_req, const int32_t* req_
                 need, ws_bytes);
   if (need > 0 && (!ws_dev || ws_bytes < need))
     return fail(KVOFF_ERANGE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
-  KVOFF_HIP(hipSetDevice(ctx->device));
+  DeviceScope dev_scope;
+  KVOFF_HIP(dev_scope.enter(ctx->device));
   st = launch_attend(ctx, b, mode, q_dev, slot_pool_dev, n_slots, block_table_dev, sel_idx_dev,
                      sel_cnt_dev, k_stride, scale, out_dev, ws_dev, (hipStream_t)stream);
   if (st) return st;
@@ -483,7 +488,8 @@ int kvoff_attention_mass(kvoff_ctx* ctx, int32_t layer, int32_t n_req, const int
     if (mode < 0) return fail(KVOFF_EINVAL, "unknown mode");
     if (k_stride < 1) return fail(KVOFF_EINVAL, "k_stride %d < 1", k_stride);
     if ((st = check_layer_offloaded(ctx, layer, b))) return st;
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     return launch_mass(ctx, b, layer, mode, q_dev, sel_idx_dev, sel_cnt_dev, k_stride, scale,
                        mass_dev, (hipStream_t)stream);
   });
@@ -493,7 +499,8 @@ int kvoff_set_kernel_timing(kvoff_ctx* ctx, int32_t on) {
   return guarded([&]() -> int {
     if (!ctx) return fail(KVOFF_EINVAL, "ctx is NULL");
     if (on && ctx->kt_ev.empty()) {
-      KVOFF_HIP(hipSetDevice(ctx->device));
+      DeviceScope dev_scope;
+      KVOFF_HIP(dev_scope.enter(ctx->device));
       ctx->kt_ev.reserve(2 * (size_t)KT_N * KT_RING);
       while (ctx->kt_ev.size() < 2 * (size_t)KT_N * KT_RING) {
         hipEvent_t e;

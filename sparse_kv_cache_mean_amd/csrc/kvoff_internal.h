@@ -125,6 +125,27 @@ namespace kvoff {
 // between calls.
 bool test_fail_alloc(const char* what);
 
+// Makes `dev` the calling thread's current device for the life of the
+// object and, if it was another one, restores that one after: a call into
+// the library leaves the caller's current device as it found it.
+class DeviceScope {
+ public:
+  hipError_t enter(int dev) {
+    hipError_t e = hipGetDevice(&prev_);
+    if (e != hipSuccess || prev_ == dev) return e;
+    e = hipSetDevice(dev);
+    switched_ = e == hipSuccess;
+    return e;
+  }
+  ~DeviceScope() {
+    if (switched_) (void)hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = -1;
+  bool switched_ = false;
+};
+
 #define KVOFF_HIP(call)                                                            \
   do {                                                                             \
     hipError_t e_ = (call);                                                        \

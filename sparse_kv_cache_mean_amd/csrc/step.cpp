@@ -82,7 +82,8 @@ extern "C" int kvoff_step(kvoff_ctx* ctx, const kvoff_step_args* A) {
 
     hipStream_t cs = (hipStream_t)A->compute_stream;
     hipStream_t xs0 = (hipStream_t)A->copy_stream;
-    KVOFF_HIP(hipSetDevice(ctx->device));
+    DeviceScope dev_scope;
+    KVOFF_HIP(dev_scope.enter(ctx->device));
     // odd layers recall on a second copy stream (the caller's, or the
     // context's own), so consecutive recalls do not queue behind each other
     hipStream_t xs1 = xs0;
