@@ -116,8 +116,8 @@ enum {
      two sets of pinned staging buffers (grown on demand) and uses them by
      turns: a set is reused once the copies of the call that used it last
      have completed.  The context's worker threads (three fewer than the
-     hardware threads, at most 10) spin for 500 us after a call before they
-     sleep. */
+     hardware threads the process may run on, at most 10) spin for 500 us
+     after a call before they sleep. */
   KVOFF_ENGINE_STAGED = 2
 };
 

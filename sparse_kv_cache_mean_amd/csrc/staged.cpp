@@ -26,6 +26,7 @@
 // alone, a recall then runs at 53.7-53.9 GB/s instead of 52.2-52.7, but
 // kvoff_step loses 3 layer-steps/s, so one stream is the default.
 #include <emmintrin.h>
+#include <sched.h>
 
 #include <algorithm>
 #include <atomic>
@@ -76,10 +77,23 @@ int stage_streams() {
   return n;
 }
 
-// worker threads of the pool: at most 10, and three hardware threads left
-// beside them (the issuing thread, which spins on the chunk counters while
-// the workers copy, and the HIP runtime's own threads).  Measured on 16
-// hardware threads, kvoff_step on the Llama-3-8B-shaped layer: 6 workers
+// hardware threads this process may run on (its affinity mask), else the
+// machine's
+int usable_cpus() {
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  if (sched_getaffinity(0, sizeof set, &set) == 0) {
+    const int n = CPU_COUNT(&set);
+    if (n > 0) return n;
+  }
+  const int hc = (int)std::thread::hardware_concurrency();
+  return hc > 0 ? hc : 4;
+}
+
+// worker threads of the pool: at most 10, and three usable hardware threads
+// left beside them (the issuing thread, which spins on the chunk counters
+// while the workers copy, and the HIP runtime's own threads).  Measured on
+// 16 hardware threads, kvoff_step on the Llama-3-8B-shaped layer: 6 workers
 // 408-411 layer-steps/s, 10 412-413, 15 (all but the issuing thread) 332-402
 // and erratic.  KVOFF_STAGE_THREADS (1..64) overrides the count for tuning.
 int stage_threads() {
@@ -87,8 +101,7 @@ int stage_threads() {
     const char* e = std::getenv("KVOFF_STAGE_THREADS");
     const int v = e ? std::atoi(e) : 0;
     if (v >= 1 && v <= 64) return v;
-    const int hc = (int)std::thread::hardware_concurrency();
-    return std::max(1, std::min(10, (hc > 0 ? hc : 4) - 3));
+    return std::max(1, std::min(10, usable_cpus() - 3));
   }();
   return n;
 }
