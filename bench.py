@@ -23,8 +23,13 @@ import platform
 import sys
 import time
 
-import numpy as np
-import torch
+# Idle OpenMP threads (the input generator's bulk fill, torch's CPU ops) go to
+# sleep instead of spinning, so they leave the host's cores to the timed run
+# that follows setup.  Set before numpy and torch load the OpenMP runtime.
+os.environ.setdefault("OMP_WAIT_POLICY", "PASSIVE")
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
